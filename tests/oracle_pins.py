@@ -1,0 +1,315 @@
+"""Pins that tie the CPU oracle to something other than itself.
+
+Every ``pin_*`` function takes the oracle module as its argument and raises
+AssertionError when the oracle disagrees with a closed form, a brute-force
+enumeration, a library routine, an invariant or a hand-worked example.
+tests/test_oracle_pins.py runs them against the oracle; the mutation test
+runs them against deliberately broken copies of it and requires that every
+copy fails at least one pin.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+from dynamic_sparse_attention_dhsa_amd.workloads import SeqSpec, make_workload
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ----------------------------------------------------------------------------- helpers (independent of the oracle)
+
+def _layout_from_lengths(seq_chunk_lens):
+    """cu_seqlens, cu_chunks, seq_chunk_start from per-sequence chunk length lists."""
+    cu_seqlens, cu_chunks, scs = [0], [0], [0]
+    for lens in seq_chunk_lens:
+        for n in lens:
+            cu_chunks.append(cu_chunks[-1] + n)
+        cu_seqlens.append(cu_chunks[-1])
+        scs.append(scs[-1] + len(lens))
+    return (np.array(cu_seqlens, np.int32), np.array(cu_chunks, np.int32), np.array(scs, np.int32))
+
+
+def _tok_chunk(cu_chunks):
+    out = []
+    for c in range(len(cu_chunks) - 1):
+        out += [c] * int(cu_chunks[c + 1] - cu_chunks[c])
+    return np.array(out, np.int64)
+
+
+def _chunk_seq(seq_chunk_start):
+    out = []
+    for b in range(len(seq_chunk_start) - 1):
+        out += [b] * int(seq_chunk_start[b + 1] - seq_chunk_start[b])
+    return np.array(out, np.int64)
+
+
+def _small_workload(seed, lens_per_seq=((5, 9, 3, 12, 7, 1, 6),), Hq=4, Hkv=2, d=8, topk=2, dtype="f32"):
+    seqs = [SeqSpec(sum(l), ("explicit", list(l)), topk, 0) for l in lens_per_seq]
+    return make_workload(seqs, Hq, Hkv, d, dtype, seed=seed)
+
+
+def _sdpa_causal_fp64(q, k, v, scale):
+    """torch's scaled_dot_product_attention on one sequence, KV heads repeated, float64 on the CPU."""
+    Hq, Hkv = q.shape[1], k.shape[1]
+    G = Hq // Hkv
+    qt = torch.from_numpy(np.ascontiguousarray(q, np.float64)).permute(1, 0, 2)
+    kt = torch.from_numpy(np.ascontiguousarray(k, np.float64)).permute(1, 0, 2).repeat_interleave(G, 0)
+    vt = torch.from_numpy(np.ascontiguousarray(v, np.float64)).permute(1, 0, 2).repeat_interleave(G, 0)
+    o = torch.nn.functional.scaled_dot_product_attention(qt[None], kt[None], vt[None], is_causal=True,
+                                                         scale=scale)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def _parse(x):
+    if x is None:
+        return float("nan")
+    if isinstance(x, str):
+        if x == "sqrt2":
+            return math.sqrt(2.0)
+        return float(Fraction(x))
+    return float(x)
+
+
+def _parse_nested(a):
+    if isinstance(a, list):
+        return [_parse_nested(b) for b in a]
+    return _parse(a)
+
+
+def load_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        g = json.load(f)
+    g["scale"] = math.log(2.0) if g["softmax_scale"] == "ln2" else float(g["softmax_scale"])
+    for key in ("q", "k", "v"):
+        g[key] = np.array(g[key], np.float32)
+    return g
+
+
+GOLDEN_FILES = ("g1_length_norm_two_heads.json", "g2_tie_lower_index.json", "g3_ragged_no_cross_sequence.json")
+
+
+# ----------------------------------------------------------------------------- pins
+
+def pin_golden(O):
+    """Hand-worked examples (tests/golden): every intermediate and final value."""
+    for name in GOLDEN_FILES:
+        g = load_golden(name)
+        ex = g["expected"]
+        r = O.prefill(g["q"], g["k"], g["v"], g["cu_seqlens"], g["cu_chunks"], g["seq_chunk_start"],
+                      np.array(g["topk"]), g["scale"])
+        np.testing.assert_allclose(r["q_sum"], np.array(_parse_nested(ex["q_sum"])), rtol=1e-6, err_msg=name)
+        np.testing.assert_allclose(r["k_sum"], np.array(_parse_nested(ex["k_sum"])), rtol=1e-6, err_msg=name)
+        np.testing.assert_allclose(r["scores"], np.array(_parse_nested(ex["scores"])), rtol=1e-6,
+                                   equal_nan=True, err_msg=name)
+        assert list(r["row_ptr"]) == ex["row_ptr"], name
+        assert r["block_idx"].tolist() == ex["block_idx"], name
+        np.testing.assert_allclose(r["out"], np.array(_parse_nested(ex["out"])), rtol=0, atol=1e-12,
+                                   err_msg=name)
+        lse_exp = np.log(np.array(_parse_nested(ex["sum_exp"])))
+        np.testing.assert_allclose(r["lse"], lse_exp, rtol=0, atol=1e-12, err_msg=name)
+
+
+def pin_summary_closed_forms(O):
+    """n = 1 is the identity; a constant chunk x gives sqrt(n) x; integer inputs match a library segment sum."""
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((9, 3, 4)).astype(np.float32)
+    assert np.array_equal(O.chunk_summaries(x, np.arange(10)), x)
+    for n in (1, 2, 3, 4, 9, 16, 100):
+        c = rng.integers(-5, 6, size=(1, 2, 4)).astype(np.float32)
+        xs = np.repeat(c, n, axis=0)
+        got = O.chunk_summaries(xs, np.array([0, n]))
+        np.testing.assert_allclose(got[0], (math.sqrt(n) * c[0].astype(np.float64)).astype(np.float32),
+                                   rtol=2e-7, atol=0)
+    lens = np.array([1, 4, 7, 2, 16, 5, 9])
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    xi = rng.integers(-8, 9, size=(cu[-1], 2, 6)).astype(np.float32)
+    seg = torch.segment_reduce(torch.from_numpy(xi.astype(np.float64)), "sum",
+                               lengths=torch.from_numpy(lens), axis=0).numpy()
+    ref = seg / np.sqrt(lens)[:, None, None]
+    np.testing.assert_allclose(O.chunk_summaries(xi, cu), ref.astype(np.float32), rtol=2e-7, atol=0)
+
+
+def pin_scores_bruteforce(O):
+    """Chunk score = (1/sqrt(n_i n_j)) * sum over token pairs of q.k, from the full token matrix; causal only."""
+    w = _small_workload(7, lens_per_seq=((3, 5, 1, 4, 6), (2, 7, 3)), Hq=4, Hkv=2, d=5)
+    q, k = w.q_f32().astype(np.float64), w.k_f32().astype(np.float64)
+    S = O.chunk_scores(O.chunk_summaries(w.q, w.cu_chunks), O.chunk_summaries(w.k, w.cu_chunks),
+                       w.seq_chunk_start)
+    tc = _tok_chunk(w.cu_chunks)
+    cseq = _chunk_seq(w.seq_chunk_start)
+    C = w.total_chunks
+    G = w.num_q_heads // w.num_kv_heads
+    for h in range(w.num_q_heads):
+        full = q[:, h, :] @ k[:, h // G, :].T
+        for i in range(C):
+            for j in range(C):
+                if cseq[i] != cseq[j] or j > i:
+                    assert np.isnan(S[h, i, j]), (h, i, j)
+                    continue
+                ni, nj = (tc == i).sum(), (tc == j).sum()
+                ref = full[np.ix_(tc == i, tc == j)].sum() / math.sqrt(ni * nj)
+                assert abs(S[h, i, j] - ref) <= 1e-5 * max(1.0, abs(ref)), (h, i, j, S[h, i, j], ref)
+
+
+def pin_topk_bruteforce(O):
+    """Kept set = the best-sum k-subset of earlier chunks, lexicographically smallest among equal sums.
+
+    Summaries are integer-valued, so scores and subset sums are exact; half the rows carry forced ties.
+    """
+    rng = np.random.default_rng(3)
+    for trial in range(6):
+        lens = [[1] * int(rng.integers(2, 10)) for _ in range(int(rng.integers(1, 3)))]
+        cu_seqlens, cu_chunks, scs = _layout_from_lengths(lens)
+        C = int(scs[-1])
+        Hq, Hkv, d = 2, 1, 3
+        lo, hi = (-1, 2) if trial % 2 else (-4, 5)          # narrow range -> many exact ties
+        qs = rng.integers(lo, hi, size=(C, Hq, d)).astype(np.float32)
+        ks = rng.integers(lo, hi, size=(C, Hkv, d)).astype(np.float32)
+        topk = rng.integers(0, 5, size=C).astype(np.int32)
+        row_ptr, bidx, _ = O.route(qs, ks, scs, topk)
+        cseq = _chunk_seq(scs)
+        for h in range(Hq):
+            for i in range(C):
+                first = int(scs[cseq[i]])
+                cand = list(range(first, i))
+                kk = min(int(topk[i]), len(cand))
+                sc = {j: int(np.dot(qs[i, h].astype(np.int64), ks[j, 0].astype(np.int64))) for j in cand}
+                best = None
+                for sub in itertools.combinations(cand, kk):
+                    key = (-sum(sc[j] for j in sub), sub)
+                    if best is None or key < best:
+                        best = key
+                want = sorted(best[1]) + [i]
+                got = bidx[h, row_ptr[i]:row_ptr[i + 1]].tolist()
+                assert got == want, (trial, h, i, got, want, sc)
+
+
+def pin_kept_invariants(O):
+    """|kept| = min(k, available) + 1, diagonal present and last, ascending, same sequence, causal."""
+    w = _small_workload(11, lens_per_seq=((4,) * 9, (2, 3, 5, 1, 1, 8), (6,)), Hq=4, Hkv=2, d=6, topk=3)
+    tk = np.array([0, 1, 2, 3, 5, 9, 2, 0, 4, 1, 3, 3, 2, 7, 3, 1], np.int32)
+    row_ptr, bidx, _ = O.route(O.chunk_summaries(w.q, w.cu_chunks), O.chunk_summaries(w.k, w.cu_chunks),
+                               w.seq_chunk_start, tk)
+    cseq = _chunk_seq(w.seq_chunk_start)
+    for h in range(w.num_q_heads):
+        for i in range(w.total_chunks):
+            row = bidx[h, row_ptr[i]:row_ptr[i + 1]].tolist()
+            first = int(w.seq_chunk_start[cseq[i]])
+            assert len(row) == min(int(tk[i]), i - first) + 1, (h, i, row)
+            assert row[-1] == i and row == sorted(set(row)), (h, i, row)
+            assert all(first <= j <= i for j in row), (h, i, row)
+
+
+def pin_dense_special_case(O):
+    """Keeping every earlier chunk gives causal dense attention (torch SDPA, float64), GQA included."""
+    w = _small_workload(5, lens_per_seq=((3, 8, 2, 5, 9), (4, 4, 1), (1,)), Hq=6, Hkv=2, d=8, topk=0)
+    big = np.full(w.total_chunks, 1000, np.int32)
+    r = O.prefill(w.q, w.k, w.v, w.cu_seqlens, w.cu_chunks, w.seq_chunk_start, big, w.softmax_scale)
+    dense_o, _ = O.dense_attention(w.q, w.k, w.v, w.cu_seqlens, w.softmax_scale)
+    for b in range(w.num_seqs):
+        s, e = w.cu_seqlens[b], w.cu_seqlens[b + 1]
+        ref = _sdpa_causal_fp64(w.q[s:e], w.k[s:e], w.v[s:e], w.softmax_scale)
+        np.testing.assert_allclose(r["out"][s:e], ref, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dense_o[s:e], ref, rtol=1e-10, atol=1e-12)
+
+
+def pin_token_level_bruteforce(O):
+    """Upsampled token importance and the kept token mask, built by loops, drive a masked dense softmax."""
+    w = _small_workload(13, lens_per_seq=((3, 6, 2, 7, 4, 5),), Hq=2, Hkv=1, d=4, topk=2)
+    r = O.prefill(w.q, w.k, w.v, w.cu_seqlens, w.cu_chunks, w.seq_chunk_start, w.topk, w.softmax_scale)
+    T = w.total_tokens
+    tc = _tok_chunk(w.cu_chunks)
+    q, k, v = (x.astype(np.float64) for x in (w.q, w.k, w.v))
+    for h in range(w.num_q_heads):
+        imp = O.token_importance(r["scores"][h], w.cu_chunks)
+        for t in range(T):
+            for u in range(T):
+                sv = r["scores"][h, tc[t], tc[u]]
+                assert (np.isnan(imp[t, u]) and np.isnan(sv)) or imp[t, u] == sv
+        # kept mask from the kept chunk lists, by loops
+        mask = np.zeros((T, T), bool)
+        for t in range(T):
+            kept = set(r["block_idx"][h, r["row_ptr"][tc[t]]:r["row_ptr"][tc[t] + 1]].tolist())
+            for u in range(t + 1):
+                mask[t, u] = tc[u] in kept
+        assert np.array_equal(mask, O.kept_token_mask(r["row_ptr"], r["block_idx"][h], w.cu_chunks))
+        logits = torch.from_numpy(w.softmax_scale * (q[:, h] @ k[:, 0].T))
+        logits = logits.masked_fill(~torch.from_numpy(mask), float("-inf"))
+        ref = (torch.softmax(logits, dim=1) @ torch.from_numpy(v[:, 0])).numpy()
+        np.testing.assert_allclose(r["out"][:, h], ref, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(r["lse"][h], torch.logsumexp(logits, dim=1).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def pin_row_sum_and_lse(O):
+    """V = 1 gives O = 1; LSE equals torch.logsumexp of the kept logits."""
+    w = _small_workload(17, lens_per_seq=((5, 2, 9, 3, 6, 4),), Hq=2, Hkv=2, d=8, topk=1)
+    ones = np.ones_like(w.v)
+    r = O.prefill(w.q, w.k, ones, w.cu_seqlens, w.cu_chunks, w.seq_chunk_start, w.topk, w.softmax_scale)
+    np.testing.assert_allclose(r["out"], 1.0, rtol=0, atol=1e-14)
+    q, k = w.q.astype(np.float64), w.k.astype(np.float64)
+    for h in range(2):
+        mask = O.kept_token_mask(r["row_ptr"], r["block_idx"][h], w.cu_chunks)
+        z = torch.from_numpy(w.softmax_scale * (q[:, h] @ k[:, h].T)).masked_fill(~torch.from_numpy(mask),
+                                                                                    float("-inf"))
+        np.testing.assert_allclose(r["lse"][h], torch.logsumexp(z, 1).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def pin_causality(O):
+    """Changing K, V after token t and Q in later chunks leaves outputs up to t bit-identical."""
+    w = _small_workload(19, lens_per_seq=((4, 6, 3, 8, 5, 2),), Hq=2, Hkv=1, d=6, topk=2)
+    base = O.prefill(w.q, w.k, w.v, w.cu_seqlens, w.cu_chunks, w.seq_chunk_start, w.topk, w.softmax_scale)
+    tc = _tok_chunk(w.cu_chunks)
+    rng = np.random.default_rng(0)
+    for t in (3, 9, 12, 19):
+        q2, k2, v2 = w.q.copy(), w.k.copy(), w.v.copy()
+        k2[t + 1:] += rng.standard_normal(k2[t + 1:].shape).astype(np.float32) * 5
+        v2[t + 1:] += rng.standard_normal(v2[t + 1:].shape).astype(np.float32) * 5
+        later = tc > tc[t]
+        q2[later] += rng.standard_normal(q2[later].shape).astype(np.float32) * 5
+        r = O.prefill(q2, k2, v2, w.cu_seqlens, w.cu_chunks, w.seq_chunk_start, w.topk, w.softmax_scale)
+        assert np.array_equal(r["out"][:t + 1], base["out"][:t + 1]), t
+        assert np.array_equal(r["lse"][:, :t + 1], base["lse"][:, :t + 1]), t
+
+
+def pin_gqa_and_permutation(O):
+    """Repeating KV heads to G = 1 changes nothing; permuting whole head groups permutes outputs."""
+    w = _small_workload(23, lens_per_seq=((3, 7, 2, 5, 6),), Hq=4, Hkv=2, d=6, topk=1)
+    base = O.prefill(w.q, w.k, w.v, w.cu_seqlens, w.cu_chunks, w.seq_chunk_start, w.topk, w.softmax_scale)
+    k_rep, v_rep = np.repeat(w.k, 2, axis=1), np.repeat(w.v, 2, axis=1)
+    rep = O.prefill(w.q, k_rep, v_rep, w.cu_seqlens, w.cu_chunks, w.seq_chunk_start, w.topk, w.softmax_scale)
+    assert np.array_equal(rep["out"], base["out"]) and np.array_equal(rep["block_idx"], base["block_idx"])
+    perm_kv = [1, 0]
+    perm_q = [2, 3, 0, 1]
+    pr = O.prefill(w.q[:, perm_q], w.k[:, perm_kv], w.v[:, perm_kv], w.cu_seqlens, w.cu_chunks,
+                   w.seq_chunk_start, w.topk, w.softmax_scale)
+    assert np.array_equal(pr["out"], base["out"][:, perm_q])
+    assert np.array_equal(pr["block_idx"], base["block_idx"][perm_q])
+
+
+def pin_ragged_equals_separate(O):
+    """A packed batch gives, sequence by sequence, what each sequence gives alone."""
+    lens = ((4, 2, 7, 3), (5,), (1, 1, 6, 2, 3, 4))
+    w = _small_workload(29, lens_per_seq=lens, Hq=2, Hkv=1, d=5, topk=2)
+    packed = O.prefill(w.q, w.k, w.v, w.cu_seqlens, w.cu_chunks, w.seq_chunk_start, w.topk, w.softmax_scale)
+    for b, l in enumerate(lens):
+        s, e = w.cu_seqlens[b], w.cu_seqlens[b + 1]
+        c0, c1 = w.seq_chunk_start[b], w.seq_chunk_start[b + 1]
+        cs1, cc1, sc1 = _layout_from_lengths([l])
+        alone = O.prefill(w.q[s:e], w.k[s:e], w.v[s:e], cs1, cc1, sc1, w.topk[c0:c1], w.softmax_scale)
+        assert np.array_equal(alone["out"], packed["out"][s:e]), b
+        for i in range(c1 - c0):
+            a = alone["block_idx"][:, alone["row_ptr"][i]:alone["row_ptr"][i + 1]] + c0
+            p = packed["block_idx"][:, packed["row_ptr"][c0 + i]:packed["row_ptr"][c0 + i + 1]]
+            assert np.array_equal(a, p), (b, i)
+
+
+ALL_PINS = [pin_golden, pin_summary_closed_forms, pin_scores_bruteforce, pin_topk_bruteforce,
+            pin_kept_invariants, pin_dense_special_case, pin_token_level_bruteforce, pin_row_sum_and_lse,
+            pin_causality, pin_gqa_and_permutation, pin_ragged_equals_separate]
