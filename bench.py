@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Throughput of the DHSA chunk-routed sparse prefill on one MI355X.
+
+One step = the whole hot path on one batch: chunk summaries (stage 1), causal
+chunk routing (stage 2) and block-sparse causal prefill (stage 3), each a
+gfx950 kernel launched through the C ABI on torch's current stream.  Inputs
+are resident in HBM before the timed region starts; the routing plan (CSR
+row pointers, a pure function of the chunk layout and the budget) is built
+on the host once, with the inputs.
+
+Default workload: the LLaMA-3.1-8B attention-layer shape at L = 131072
+(32 query heads, 8 KV heads, head_dim 128, bf16), chunk lengths uniform in
+[64, 512], top-32 earlier chunks plus the diagonal, 256 planted needles.
+
+Prints one JSON line with the throughput, a roofline object for the
+dominant kernel (stage 3, MFMA bf16 against the kept FLOPs), per-stage
+figures, and the CPU oracle timed on a bounded sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse-prefill tokens/s per attn layer at 128K (8B shape); % MFMA/HBM peak"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PREFILL_SRC = os.path.join(ROOT, "dynamic_sparse_attention_dhsa_amd", "csrc", "prefill_bf16.hip")
+
+
+def kept_flops(block_idx: np.ndarray, row_ptr: np.ndarray, cu_chunks: np.ndarray, d: int) -> float:
+    """Algorithmic FLOPs of stage 3: 4*d per kept (query, key) pair (QK^T and PV, 2 FLOPs per MAC)."""
+    lens = np.diff(cu_chunks).astype(np.int64)
+    C = lens.size
+    total = 0
+    row_of = np.repeat(np.arange(C), np.diff(row_ptr))
+    for h in range(block_idx.shape[0]):
+        kept = block_idx[h].astype(np.int64)
+        diag = kept == row_of
+        off = np.bincount(row_of[~diag], weights=lens[kept[~diag]], minlength=C)
+        total += float((lens * off).sum() + (lens * (lens + 1) // 2).sum())
+    return 4.0 * d * total
+
+
+def stage_bytes(T, C, Hq, Hkv, d, s, nnz):
+    b1 = T * (Hq + Hkv) * d * s + C * (Hq + Hkv) * d * 4
+    b2 = C * (Hq + Hkv) * d * 4 + (C + 1) * 4 + Hq * nnz * 4
+    return b1, b2
+
+
+def traffic_record(workload: str):
+    """HBM traffic of stage 3 from committed rocprofv3 counter runs, if they match the kernel source."""
+    path = os.path.join(ROOT, "profiles", f"prefill_bf16_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src_hash = hashlib.sha256(open(PREFILL_SRC, "rb").read()).hexdigest()[:16]
+    if rec.get("kernel_source_sha256_16") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, topk, budget_s: float):
+    """The CPU oracle (as it stands) on a bounded sample of the same workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    qf, kf, vf = w.q_f32(), w.k_f32(), w.v_f32()
+    t0 = time.perf_counter()
+    qs = oracle.chunk_summaries(qf, w.cu_chunks)
+    ks = oracle.chunk_summaries(kf, w.cu_chunks)
+    t_sum = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    rp, bi, _ = oracle.route(qs, ks, w.seq_chunk_start, topk)
+    t_route = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    rows = [(int(rng.integers(w.num_q_heads)), int(rng.integers(w.total_chunks))) for _ in range(4096)]
+    lens = np.diff(w.cu_chunks)
+    done_tok = 0
+    t_att = 0.0
+    n_rows = 0
+    for h, i in rows:
+        t0 = time.perf_counter()
+        oracle.attend(qf, kf, vf, w.cu_chunks, rp, bi, w.softmax_scale, heads=[h], chunks=[i])
+        t_att += time.perf_counter() - t0
+        done_tok += int(lens[i])
+        n_rows += 1
+        if t_att + t_sum + t_route > budget_s:
+            break
+    per_token_head = t_att / done_tok
+    t_att_full = per_token_head * w.total_tokens * w.num_q_heads
+    t_full = t_sum + t_route + t_att_full
+    return {"value": w.total_tokens / t_full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"oracle summaries + routing of the whole workload ({t_sum + t_route:.1f} s), attention "
+                       f"on {n_rows} random (head, chunk) rows = {done_tok} query-token-heads of "
+                       f"{w.total_tokens * w.num_q_heads} ({t_att:.1f} s), attention time extrapolated per "
+                       f"query-token-head; fp64 numpy"),
+            "seconds_est_full_step": t_full}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, help="named workload 0..4 (3 = 128K headline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for the baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus} GPUs).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import dynamic_sparse_attention_dhsa_amd as D
+    from dynamic_sparse_attention_dhsa_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    print(f"[bench] generating workload {args.config}", file=sys.stderr, flush=True)
+    w = W.make_config(args.config)
+    bf16 = w.dtype == "bf16"
+    tdt = torch.bfloat16 if bf16 else torch.float32
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16) if bf16 else torch.from_numpy(a).cuda()
+
+    q, k, v = dev(w.q), dev(w.k), dev(w.v)
+    T, C, Hq, Hkv, d = w.total_tokens, w.total_chunks, w.num_q_heads, w.num_kv_heads, w.head_dim
+    layout = D.Layout(w.cu_seqlens, w.cu_chunks, w.seq_chunk_start, Hq, Hkv, d, tdt)
+    plan = D.RoutePlan(layout, w.topk)
+    q_sum = torch.empty((C, Hq, d), dtype=torch.float32, device="cuda")
+    k_sum = torch.empty((C, Hkv, d), dtype=torch.float32, device="cuda")
+    block_idx = torch.empty((Hq, plan.nnz), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        D.chunk_summarize(layout, q, k, q_sum, k_sum)
+        if ev is not None:
+            ev[1].record(stream)
+        D.route(layout, plan, q_sum, k_sum, block_idx)
+        if ev is not None:
+            ev[2].record(stream)
+        D.sparse_prefill(layout, plan, q, k, v, block_idx, w.softmax_scale, out=out)
+        if ev is not None:
+            ev[3].record(stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    print(f"[bench] timed {args.steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
+
+    t1 = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
+    t2 = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
+    t3 = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e-3
+
+    bidx = block_idx.cpu().numpy()
+    F3 = kept_flops(bidx, plan.h_row_ptr, w.cu_chunks, d)
+    b1, b2 = stage_bytes(T, C, Hq, Hkv, d, 2 if bf16 else 4, plan.nnz)
+    causal_pairs = float(sum(((n := int(w.cu_seqlens[b + 1] - w.cu_seqlens[b])) * (n + 1)) // 2
+                             for b in range(w.num_seqs))) * Hq
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
+    achieved = F3 / t3 / 1e12
+    ms_per_step = elapsed / args.steps * 1e3
+    result = {
+        "metric": METRIC,
+        "value": T * args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": T, "num_seqs": w.num_seqs, "num_q_heads": Hq,
+                   "num_kv_heads": Hkv, "head_dim": d, "chunks": C,
+                   "topk": int(w.topk.max()) if C else 0, "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel" if bf16 else "prefill_f32_kernel",
+                     "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": traffic_record(w.name) if bf16 else None,
+                     "algorithmic_flops_per_launch": F3},
+        "stages": {
+            "t_summarize_ms": t1 * 1e3, "t_route_ms": t2 * 1e3, "t_prefill_ms": t3 * 1e3,
+            "summarize_GBps": b1 / t1 / 1e9, "route_GBps": b2 / t2 / 1e9,
+            "stages12_hbm_frac": (b1 + b2) / (t1 + t2) / 1e9 / PEAK_HBM_GBS,
+            "bytes_stage1": b1, "bytes_stage2": b2,
+            "kept_density_vs_causal": F3 / (4.0 * d * causal_pairs),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, w.topk, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

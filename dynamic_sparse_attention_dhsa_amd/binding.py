@@ -1,0 +1,229 @@
+"""Python binding of the DHSA C ABI (include/dhsa.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream, every stage runs in the gfx950 kernels of ``libdhsa.so``.  There is
+no fallback: if the library is missing or a tensor is not on the GPU, these
+functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdhsa.so")
+
+DHSA_OK = 0
+DHSA_F32 = 0
+DHSA_BF16 = 1
+STATUS_NAMES = {0: "DHSA_OK", 1: "DHSA_ERR_NULL_ARG", 2: "DHSA_ERR_BAD_SHAPE", 3: "DHSA_ERR_BAD_LAYOUT",
+                4: "DHSA_ERR_BAD_BUDGET", 5: "DHSA_ERR_UNSUPPORTED", 6: "DHSA_ERR_LAUNCH"}
+
+# every entry point declared in include/dhsa.h
+EXPORTS = ("dhsa_abi_version", "dhsa_status_str", "dhsa_validate_layout", "dhsa_route_plan",
+           "dhsa_chunk_summarize", "dhsa_route", "dhsa_sparse_prefill")
+
+
+class DhsaError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        super().__init__(f"{where}: {message}")
+        self.status = status
+        self.name = STATUS_NAMES.get(status, str(status))
+
+
+class LayoutStruct(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("total_tokens", ctypes.c_int32),
+                ("total_chunks", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("cu_seqlens", ctypes.c_void_p), ("cu_chunks", ctypes.c_void_p),
+                ("seq_chunk_start", ctypes.c_void_p), ("h_cu_seqlens", ctypes.c_void_p),
+                ("h_cu_chunks", ctypes.c_void_p), ("h_seq_chunk_start", ctypes.c_void_p)]
+
+
+_LIB = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libdhsa.so (after torch, so both share torch's HIP runtime)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with dynamic_sparse_attention_dhsa_amd.build.build()")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lp = ctypes.POINTER(LayoutStruct)
+    lib.dhsa_abi_version.restype = i32
+    lib.dhsa_status_str.restype = ctypes.c_char_p
+    lib.dhsa_status_str.argtypes = [i32]
+    lib.dhsa_validate_layout.restype = i32
+    lib.dhsa_validate_layout.argtypes = [lp]
+    lib.dhsa_route_plan.restype = i32
+    lib.dhsa_route_plan.argtypes = [lp, vp, vp, ctypes.POINTER(i64)]
+    lib.dhsa_chunk_summarize.restype = i32
+    lib.dhsa_chunk_summarize.argtypes = [lp, vp, vp, vp, vp, vp]
+    lib.dhsa_route.restype = i32
+    lib.dhsa_route.argtypes = [lp, vp, vp, vp, vp, i64, vp, vp]
+    lib.dhsa_sparse_prefill.restype = i32
+    lib.dhsa_sparse_prefill.argtypes = [lp, vp, vp, vp, vp, vp, i64, vp, ctypes.c_float, vp, vp, vp]
+    if lib.dhsa_abi_version() != 1:
+        raise RuntimeError("libdhsa.so ABI version mismatch")
+    _LIB = lib
+    return lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != DHSA_OK:
+        msg = load_library().dhsa_status_str(status).decode()
+        raise DhsaError(status, where, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _host_i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+class Layout:
+    """A packed varlen batch: device offsets plus their host mirrors, as the C ABI wants them."""
+
+    def __init__(self, cu_seqlens, cu_chunks, seq_chunk_start, num_q_heads: int, num_kv_heads: int,
+                 head_dim: int, dtype: torch.dtype, device="cuda"):
+        self.h_cu_seqlens = _host_i32(cu_seqlens)
+        self.h_cu_chunks = _host_i32(cu_chunks)
+        self.h_seq_chunk_start = _host_i32(seq_chunk_start)
+        if dtype == torch.bfloat16:
+            code = DHSA_BF16
+        elif dtype == torch.float32:
+            code = DHSA_F32
+        else:
+            raise DhsaError(5, "Layout", f"unsupported dtype {dtype}")
+        self.dtype = dtype
+        self.device = torch.device(device)
+        self.d_cu_seqlens = torch.from_numpy(self.h_cu_seqlens).to(self.device)
+        self.d_cu_chunks = torch.from_numpy(self.h_cu_chunks).to(self.device)
+        self.d_seq_chunk_start = torch.from_numpy(self.h_seq_chunk_start).to(self.device)
+        self.num_seqs = self.h_cu_seqlens.size - 1
+        self.total_tokens = int(self.h_cu_seqlens[-1])
+        self.total_chunks = int(self.h_cu_chunks.size - 1)
+        self.num_q_heads, self.num_kv_heads, self.head_dim = num_q_heads, num_kv_heads, head_dim
+        self.struct = LayoutStruct(self.num_seqs, self.total_tokens, self.total_chunks, num_q_heads,
+                                   num_kv_heads, head_dim, code, self.d_cu_seqlens.data_ptr(),
+                                   self.d_cu_chunks.data_ptr(), self.d_seq_chunk_start.data_ptr(),
+                                   self.h_cu_seqlens.ctypes.data, self.h_cu_chunks.ctypes.data,
+                                   self.h_seq_chunk_start.ctypes.data)
+
+    def validate(self) -> None:
+        _check(load_library().dhsa_validate_layout(ctypes.byref(self.struct)), "dhsa_validate_layout")
+
+    def _check_tensor(self, t: torch.Tensor, heads: int, name: str) -> None:
+        if not t.is_cuda:
+            raise DhsaError(1, name, "tensor is not on the GPU")
+        if t.dtype != self.dtype:
+            raise DhsaError(2, name, f"dtype {t.dtype} != layout dtype {self.dtype}")
+        if tuple(t.shape) != (self.total_tokens, heads, self.head_dim) or not t.is_contiguous():
+            raise DhsaError(2, name, f"expected contiguous [{self.total_tokens}, {heads}, {self.head_dim}], "
+                                     f"got {tuple(t.shape)}")
+
+
+class RoutePlan:
+    """CSR row pointers (host and device) for a per-chunk budget."""
+
+    def __init__(self, layout: Layout, topk):
+        lib = load_library()
+        self.h_topk = _host_i32(topk)
+        if self.h_topk.shape != (layout.total_chunks,):
+            raise DhsaError(2, "route_plan", "topk needs one entry per chunk")
+        self.h_row_ptr = np.zeros(layout.total_chunks + 1, np.int32)
+        nnz = ctypes.c_int64(0)
+        _check(lib.dhsa_route_plan(ctypes.byref(layout.struct), self.h_topk.ctypes.data,
+                                   self.h_row_ptr.ctypes.data, ctypes.byref(nnz)), "dhsa_route_plan")
+        self.nnz = int(nnz.value)
+        self.d_row_ptr = torch.from_numpy(self.h_row_ptr).to(layout.device)
+
+    @classmethod
+    def from_row_ptr(cls, layout: Layout, row_ptr) -> "RoutePlan":
+        self = cls.__new__(cls)
+        self.h_topk = None
+        self.h_row_ptr = _host_i32(row_ptr)
+        self.nnz = int(self.h_row_ptr[-1])
+        self.d_row_ptr = torch.from_numpy(self.h_row_ptr).to(layout.device)
+        return self
+
+
+def chunk_summarize(layout: Layout, q: torch.Tensor, k: torch.Tensor,
+                    q_sum: Optional[torch.Tensor] = None, k_sum: Optional[torch.Tensor] = None
+                    ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Stage 1 (dhsa_chunk_summarize): fp32 q_sum [C, Hq, d], k_sum [C, Hkv, d]."""
+    layout._check_tensor(q, layout.num_q_heads, "q")
+    layout._check_tensor(k, layout.num_kv_heads, "k")
+    C = layout.total_chunks
+    if q_sum is None:
+        q_sum = torch.empty((C, layout.num_q_heads, layout.head_dim), dtype=torch.float32, device=q.device)
+    if k_sum is None:
+        k_sum = torch.empty((C, layout.num_kv_heads, layout.head_dim), dtype=torch.float32, device=q.device)
+    _check(load_library().dhsa_chunk_summarize(ctypes.byref(layout.struct), _ptr(q), _ptr(k), _ptr(q_sum),
+                                               _ptr(k_sum), _stream()), "dhsa_chunk_summarize")
+    return q_sum, k_sum
+
+
+def route(layout: Layout, plan: RoutePlan, q_sum: torch.Tensor, k_sum: torch.Tensor,
+          block_idx: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Stage 2 (dhsa_route): kept key chunks, int32 [Hq, nnz], rows ascending with the diagonal last."""
+    if block_idx is None:
+        block_idx = torch.empty((layout.num_q_heads, plan.nnz), dtype=torch.int32, device=q_sum.device)
+    for t, name in ((q_sum, "q_sum"), (k_sum, "k_sum")):
+        if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
+            raise DhsaError(2, name, "expected a contiguous float32 GPU tensor")
+    _check(load_library().dhsa_route(ctypes.byref(layout.struct), _ptr(q_sum), _ptr(k_sum), _ptr(plan.d_row_ptr),
+                                     plan.h_row_ptr.ctypes.data, plan.nnz, _ptr(block_idx), _stream()),
+           "dhsa_route")
+    return block_idx
+
+
+def sparse_prefill(layout: Layout, plan: RoutePlan, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                   block_idx: torch.Tensor, softmax_scale: Optional[float] = None, return_lse: bool = False,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Stage 3 (dhsa_sparse_prefill): out [T, Hq, d] in q's dtype, optional lse [Hq, T] fp32."""
+    layout._check_tensor(q, layout.num_q_heads, "q")
+    layout._check_tensor(k, layout.num_kv_heads, "k")
+    layout._check_tensor(v, layout.num_kv_heads, "v")
+    if block_idx.dtype != torch.int32 or not block_idx.is_cuda or tuple(block_idx.shape) != (layout.num_q_heads,
+                                                                                              plan.nnz):
+        raise DhsaError(2, "block_idx", f"expected int32 GPU tensor [{layout.num_q_heads}, {plan.nnz}]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(layout.head_dim)
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((layout.num_q_heads, layout.total_tokens), dtype=torch.float32, device=q.device)
+    _check(load_library().dhsa_sparse_prefill(ctypes.byref(layout.struct), _ptr(q), _ptr(k), _ptr(v),
+                                              _ptr(plan.d_row_ptr), plan.h_row_ptr.ctypes.data, plan.nnz,
+                                              _ptr(block_idx), float(softmax_scale), _ptr(out), _ptr(lse),
+                                              _stream()), "dhsa_sparse_prefill")
+    return (out, lse) if return_lse else out
+
+
+def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens, cu_chunks, seq_chunk_start, topk,
+            softmax_scale: Optional[float] = None, return_lse: bool = False):
+    """The whole path: summaries, routing, sparse attention.  Returns a dict of device tensors."""
+    layout = Layout(cu_seqlens, cu_chunks, seq_chunk_start, q.shape[1], k.shape[1], q.shape[2], q.dtype,
+                    device=q.device)
+    plan = RoutePlan(layout, topk)
+    q_sum, k_sum = chunk_summarize(layout, q, k)
+    block_idx = route(layout, plan, q_sum, k_sum)
+    res = sparse_prefill(layout, plan, q, k, v, block_idx, softmax_scale, return_lse=return_lse)
+    out, lse = res if return_lse else (res, None)
+    return dict(out=out, lse=lse, q_sum=q_sum, k_sum=k_sum, row_ptr=plan.h_row_ptr, block_idx=block_idx,
+                layout=layout, plan=plan)

@@ -1,0 +1,168 @@
+// C ABI of the DHSA sparse-prefill library: host-side validation, planning
+// and dispatch to the gfx950 kernels.  Nothing here allocates device memory or
+// synchronises; every failure is reported before any kernel is enqueued.
+#include <math.h>
+
+#include "dhsa_internal.hpp"
+
+using dhsa::Plan;
+
+namespace {
+
+bool head_dim_supported(int32_t dtype, int32_t d) {
+  if (dtype == DHSA_BF16) return d == 64 || d == 128 || d == 256;
+  if (dtype == DHSA_F32) return d == 32 || d == 64 || d == 128;
+  return false;
+}
+
+// Validates the layout from its host mirrors and fills `plan`.
+dhsa_status check_layout(const dhsa_layout* L, Plan* plan) {
+  if (L == nullptr) return DHSA_ERR_NULL_ARG;
+  if (L->num_seqs < 0 || L->total_tokens < 0 || L->total_chunks < 0 || L->num_q_heads < 1 ||
+      L->num_kv_heads < 1 || L->head_dim < 1)
+    return DHSA_ERR_BAD_SHAPE;
+  if (L->num_q_heads % L->num_kv_heads != 0) return DHSA_ERR_BAD_SHAPE;
+  if (L->dtype != DHSA_F32 && L->dtype != DHSA_BF16) return DHSA_ERR_UNSUPPORTED;
+  if (!head_dim_supported(L->dtype, L->head_dim)) return DHSA_ERR_UNSUPPORTED;
+  if (L->h_cu_seqlens == nullptr || L->h_cu_chunks == nullptr || L->h_seq_chunk_start == nullptr)
+    return DHSA_ERR_NULL_ARG;
+  if (L->cu_seqlens == nullptr || L->cu_chunks == nullptr || L->seq_chunk_start == nullptr)
+    return DHSA_ERR_NULL_ARG;
+  const int32_t B = L->num_seqs, C = L->total_chunks, T = L->total_tokens;
+  const int32_t* cs = L->h_cu_seqlens;
+  const int32_t* cc = L->h_cu_chunks;
+  const int32_t* sc = L->h_seq_chunk_start;
+  if (cs[0] != 0 || sc[0] != 0 || cc[0] != 0) return DHSA_ERR_BAD_LAYOUT;
+  if (cs[B] != T || sc[B] != C || cc[C] != T) return DHSA_ERR_BAD_LAYOUT;
+  int32_t max_len = 0, max_per_seq = 0;
+  for (int32_t c = 0; c < C; ++c) {
+    const int32_t n = cc[c + 1] - cc[c];
+    if (n < 1) return DHSA_ERR_BAD_LAYOUT;
+    if (n > max_len) max_len = n;
+  }
+  for (int32_t b = 0; b < B; ++b)    // monotone, so every seq_chunk_start entry lies in [0, C]
+    if (cs[b + 1] < cs[b] || sc[b + 1] < sc[b]) return DHSA_ERR_BAD_LAYOUT;
+  for (int32_t b = 0; b < B; ++b) {
+    if (cc[sc[b]] != cs[b] || cc[sc[b + 1]] != cs[b + 1]) return DHSA_ERR_BAD_LAYOUT;
+    const int32_t nc = sc[b + 1] - sc[b];
+    if (nc > max_per_seq) max_per_seq = nc;
+  }
+  if (max_per_seq > DHSA_MAX_CHUNKS_PER_SEQ) return DHSA_ERR_UNSUPPORTED;
+  if (plan != nullptr) {
+    *plan = Plan{B, T, C, L->num_q_heads, L->num_kv_heads, L->head_dim, L->dtype,
+                 L->cu_seqlens, L->cu_chunks, L->seq_chunk_start, max_len, max_per_seq};
+  }
+  return DHSA_OK;
+}
+
+// Row pointers must be the plan of some budget: row i holds between 1 and i_loc + 1 entries.
+// Sets *wide when a row keeps more than 64 earlier chunks without keeping all of them.
+dhsa_status check_row_ptr(const dhsa_layout* L, const int32_t* h_row_ptr, int64_t nnz, bool* wide) {
+  if (h_row_ptr == nullptr) return DHSA_ERR_NULL_ARG;
+  const int32_t* sc = L->h_seq_chunk_start;
+  if (h_row_ptr[0] != 0) return DHSA_ERR_BAD_SHAPE;
+  *wide = false;
+  for (int32_t b = 0; b < L->num_seqs; ++b) {
+    for (int32_t c = sc[b]; c < sc[b + 1]; ++c) {
+      const int64_t len = (int64_t)h_row_ptr[c + 1] - h_row_ptr[c];
+      const int32_t i_loc = c - sc[b];
+      if (len < 1 || len > (int64_t)i_loc + 1) return DHSA_ERR_BAD_SHAPE;
+      if (len - 1 > 64 && len - 1 < i_loc) *wide = true;
+    }
+  }
+  if ((int64_t)h_row_ptr[L->total_chunks] != nnz) return DHSA_ERR_BAD_SHAPE;
+  return DHSA_OK;
+}
+
+dhsa_status launched(hipError_t e) { return e == hipSuccess ? DHSA_OK : DHSA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t dhsa_abi_version(void) { return DHSA_ABI_VERSION; }
+
+const char* dhsa_status_str(int32_t status) {
+  switch (status) {
+    case DHSA_OK: return "DHSA_OK";
+    case DHSA_ERR_NULL_ARG: return "DHSA_ERR_NULL_ARG: a required pointer is NULL";
+    case DHSA_ERR_BAD_SHAPE: return "DHSA_ERR_BAD_SHAPE: inconsistent sizes or row pointers";
+    case DHSA_ERR_BAD_LAYOUT: return "DHSA_ERR_BAD_LAYOUT: chunk/sequence offsets are invalid";
+    case DHSA_ERR_BAD_BUDGET: return "DHSA_ERR_BAD_BUDGET: negative key-chunk budget";
+    case DHSA_ERR_UNSUPPORTED: return "DHSA_ERR_UNSUPPORTED: dtype, head_dim or chunk count not supported";
+    case DHSA_ERR_LAUNCH: return "DHSA_ERR_LAUNCH: kernel launch failed";
+    default: return "unknown dhsa_status";
+  }
+}
+
+dhsa_status dhsa_validate_layout(const dhsa_layout* layout) { return check_layout(layout, nullptr); }
+
+dhsa_status dhsa_route_plan(const dhsa_layout* layout, const int32_t* h_topk, int32_t* h_row_ptr,
+                            int64_t* nnz) {
+  dhsa_status st = check_layout(layout, nullptr);
+  if (st != DHSA_OK) return st;
+  if (h_topk == nullptr || h_row_ptr == nullptr || nnz == nullptr) return DHSA_ERR_NULL_ARG;
+  const int32_t* sc = layout->h_seq_chunk_start;
+  for (int32_t c = 0; c < layout->total_chunks; ++c)
+    if (h_topk[c] < 0) return DHSA_ERR_BAD_BUDGET;
+  int64_t acc = 0;
+  h_row_ptr[0] = 0;
+  for (int32_t b = 0; b < layout->num_seqs; ++b) {
+    for (int32_t c = sc[b]; c < sc[b + 1]; ++c) {
+      const int32_t i_loc = c - sc[b];
+      acc += (int64_t)(h_topk[c] < i_loc ? h_topk[c] : i_loc) + 1;
+      if (acc > 0x7fffffffLL) return DHSA_ERR_BAD_SHAPE;
+      h_row_ptr[c + 1] = (int32_t)acc;
+    }
+  }
+  *nnz = acc;
+  return DHSA_OK;
+}
+
+dhsa_status dhsa_chunk_summarize(const dhsa_layout* layout, const void* q, const void* k, float* q_sum,
+                                 float* k_sum, void* stream) {
+  Plan p;
+  dhsa_status st = check_layout(layout, &p);
+  if (st != DHSA_OK) return st;
+  if (p.C == 0) return DHSA_OK;
+  if (q == nullptr || k == nullptr || q_sum == nullptr || k_sum == nullptr) return DHSA_ERR_NULL_ARG;
+  return launched(dhsa::launch_summarize(p, q, k, q_sum, k_sum, (hipStream_t)stream));
+}
+
+dhsa_status dhsa_route(const dhsa_layout* layout, const float* q_sum, const float* k_sum,
+                       const int32_t* row_ptr, const int32_t* h_row_ptr, int64_t nnz, int32_t* block_idx,
+                       void* stream) {
+  Plan p;
+  dhsa_status st = check_layout(layout, &p);
+  if (st != DHSA_OK) return st;
+  bool wide = false;
+  st = check_row_ptr(layout, h_row_ptr, nnz, &wide);
+  if (st != DHSA_OK) return st;
+  if (p.C == 0) return DHSA_OK;
+  if (q_sum == nullptr || k_sum == nullptr || row_ptr == nullptr || block_idx == nullptr)
+    return DHSA_ERR_NULL_ARG;
+  return launched(dhsa::launch_route(p, q_sum, k_sum, row_ptr, nnz, block_idx, wide, (hipStream_t)stream));
+}
+
+dhsa_status dhsa_sparse_prefill(const dhsa_layout* layout, const void* q, const void* k, const void* v,
+                                const int32_t* row_ptr, const int32_t* h_row_ptr, int64_t nnz,
+                                const int32_t* block_idx, float softmax_scale, void* out, float* lse,
+                                void* stream) {
+  Plan p;
+  dhsa_status st = check_layout(layout, &p);
+  if (st != DHSA_OK) return st;
+  bool wide = false;
+  st = check_row_ptr(layout, h_row_ptr, nnz, &wide);
+  if (st != DHSA_OK) return st;
+  if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return DHSA_ERR_BAD_SHAPE;
+  if (p.C == 0) return DHSA_OK;
+  if (q == nullptr || k == nullptr || v == nullptr || row_ptr == nullptr || block_idx == nullptr ||
+      out == nullptr)
+    return DHSA_ERR_NULL_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (p.dtype == DHSA_BF16)
+    return launched(dhsa::launch_prefill_bf16(p, q, k, v, row_ptr, nnz, block_idx, softmax_scale, out, lse, s));
+  return launched(dhsa::launch_prefill_f32(p, q, k, v, row_ptr, nnz, block_idx, softmax_scale, out, lse, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Internal declarations shared by the C-ABI layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dhsa.h"
+
+#define DHSA_MAX_WORDS (DHSA_MAX_CHUNKS_PER_SEQ / 32)
+
+namespace dhsa {
+
+// Layout facts derived on the host from the validated host mirrors.
+struct Plan {
+  int32_t B, T, C, Hq, Hkv, d, dtype;
+  const int32_t* cu_seqlens;       // device
+  const int32_t* cu_chunks;        // device
+  const int32_t* seq_chunk_start;  // device
+  int32_t max_chunk_len;           // longest chunk (tokens)
+  int32_t max_chunks_per_seq;      // most chunks in one sequence
+};
+
+// Stage 1: q_sum / k_sum (fp32).
+hipError_t launch_summarize(const Plan& p, const void* q, const void* k, float* q_sum, float* k_sum,
+                            hipStream_t stream);
+
+// Stage 2: kept key-chunk lists.  `wide_rows` tells whether some row keeps more than 64 earlier
+// chunks while not keeping all of them (those rows take the general sorting kernel).
+hipError_t launch_route(const Plan& p, const float* q_sum, const float* k_sum, const int32_t* row_ptr,
+                        int64_t nnz, int32_t* block_idx, bool wide_rows, hipStream_t stream);
+
+// Stage 3: block-sparse causal prefill.
+hipError_t launch_prefill_bf16(const Plan& p, const void* q, const void* k, const void* v,
+                               const int32_t* row_ptr, int64_t nnz, const int32_t* block_idx,
+                               float softmax_scale, void* out, float* lse, hipStream_t stream);
+hipError_t launch_prefill_f32(const Plan& p, const void* q, const void* k, const void* v,
+                              const int32_t* row_ptr, int64_t nnz, const int32_t* block_idx,
+                              float softmax_scale, void* out, float* lse, hipStream_t stream);
+
+// Device helpers ----------------------------------------------------------------------------
+
+// Index of the sequence containing chunk c: the last b with seq_chunk_start[b] <= c.
+__device__ inline int seq_of_chunk(const int32_t* __restrict__ seq_chunk_start, int B, int c) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (seq_chunk_start[mid] <= c) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace dhsa

@@ -1,0 +1,300 @@
+// Stage 2: causal chunk routing on gfx950.
+//
+// "Long-Context Modeling with Dynamic Hierarchical Sparse Attention for
+// On-Device LLMs" (Abstract): chunk-level similarity scores, upsampled to token
+// level, decide which token interactions are kept; the ICML 2026 page
+// (Abstract) makes the routing causal.  With a budget counted in chunks the
+// broadcast of chunk scores to token pairs keeps whole chunks, so a row
+// (q head h, query chunk i) keeps
+//   the top-k earlier chunks j of its sequence by s_j = q_sum[i,h] . k_sum[j,h/G],
+//   ranked by (s_j descending, j ascending), plus the diagonal chunk i,
+// written ascending into its slice of the CSR block list.
+//
+// Ranking uses a 64-bit key (order-preserving bits of the fp32 score, then
+// the complemented chunk id), so a larger key is a better candidate and every
+// key is distinct: ties resolve to the lower chunk id exactly.
+//
+// Main kernel: a wave owns one q head and four consecutive query chunks.  It
+// walks the candidates in batches of 64 (one per lane), computes the four
+// rows' fp32 dot products, and keeps each row's best 64 keys as a sorted
+// wave-wide list: a batch is bitonic-sorted across lanes, merged with the list
+// by an element-wise max against the reversed order, and re-sorted with a
+// bitonic half-cleaner cascade.  Batches that cannot beat the row's current
+// k-th key are skipped.  Rows keeping more than 64 chunks out of a longer
+// candidate list go to a general kernel that bitonic-sorts all of the row's
+// keys in LDS.
+#include "dhsa_internal.hpp"
+
+namespace dhsa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kRowsPerWave = 4;
+constexpr int kMaxTop = 64;
+constexpr int kWideThreads = 256;
+constexpr int kMaxCand = 8192;
+
+__device__ inline uint32_t ordered_bits(float s) {
+  uint32_t u = (s == 0.0f) ? 0u : __float_as_uint(s);   // -0 and +0 rank equal
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ inline uint64_t rank_key(float s, int j) {
+  return ((uint64_t)ordered_bits(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+}
+
+__device__ inline int key_chunk(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
+
+__device__ inline uint64_t shfl_xor_u64(uint64_t x, int m) {
+  uint32_t lo = __shfl_xor((unsigned)x, m);
+  uint32_t hi = __shfl_xor((unsigned)(x >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ inline uint64_t shfl_u64(uint64_t x, int src) {
+  uint32_t lo = __shfl((unsigned)x, src);
+  uint32_t hi = __shfl((unsigned)(x >> 32), src);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Bitonic sort of one key per lane across the wave; ascending (lane 0 smallest)
+// when `ascending`, else descending.
+__device__ inline uint64_t wave_sort(uint64_t key, int lane, bool ascending) {
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      uint64_t other = shfl_xor_u64(key, stride);
+      bool lower = (lane & stride) == 0;
+      bool block_up = ((lane & size) == 0) == ascending;   // direction of this block
+      bool keep_small = (lower == block_up);
+      key = keep_small ? (key < other ? key : other) : (key > other ? key : other);
+    }
+  }
+  return key;
+}
+
+__device__ inline uint32_t wave_sort_u32_asc(uint32_t v, int lane) {
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      uint32_t other = __shfl_xor(v, stride);
+      bool lower = (lane & stride) == 0;
+      bool block_up = (lane & size) == 0;
+      bool keep_small = (lower == block_up);
+      v = keep_small ? min(v, other) : max(v, other);
+    }
+  }
+  return v;
+}
+
+// `top` is sorted descending across lanes; returns the best 64 of top U batch, sorted descending.
+__device__ inline uint64_t merge_batch(uint64_t top, uint64_t batch, int lane) {
+  uint64_t b = wave_sort(batch, lane, /*ascending=*/true);
+  uint64_t m = top > b ? top : b;                 // bitonic: falls, then rises
+#pragma unroll
+  for (int stride = 32; stride > 0; stride >>= 1) {
+    uint64_t other = shfl_xor_u64(m, stride);
+    bool lower = (lane & stride) == 0;
+    m = lower ? (m > other ? m : other) : (m < other ? m : other);
+  }
+  return m;
+}
+
+template <int D>
+__global__ __launch_bounds__(kWaves * 64) void route_kernel(
+    const float* __restrict__ q_sum, const float* __restrict__ k_sum,
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ seq_chunk_start,
+    int32_t* __restrict__ block_idx, int B, int C, int Hq, int Hkv, long long nnz) {
+  __shared__ float qs[kWaves][kRowsPerWave][D];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.y * kWaves + wave;
+  const int i0 = blockIdx.x * kRowsPerWave;
+  const int G = Hq / Hkv;
+  if (h >= Hq) return;                       // whole wave leaves; no block barrier below
+  const int g = h / G;
+
+  int first[kRowsPerWave], kk[kRowsPerWave], nc[kRowsPerWave];
+  bool select[kRowsPerWave];
+  int jmin = 0x7fffffff, jend = 0;
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; ++r) {
+    const int i = i0 + r;
+    if (i < C) {
+      first[r] = seq_chunk_start[seq_of_chunk(seq_chunk_start, B, i)];
+      nc[r] = i - first[r];
+      kk[r] = row_ptr[i + 1] - row_ptr[i] - 1;
+      select[r] = kk[r] > 0 && kk[r] < nc[r] && kk[r] <= kMaxTop;
+      if (select[r]) { jmin = min(jmin, first[r]); jend = max(jend, i); }
+    } else {
+      first[r] = 0; nc[r] = 0; kk[r] = 0; select[r] = false;
+    }
+    for (int x = lane; x < D; x += 64)
+      qs[wave][r][x] = (i < C) ? q_sum[((size_t)i * Hq + h) * D + x] : 0.f;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  uint64_t top[kRowsPerWave];
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; ++r) top[r] = 0;
+
+  for (int jb = jmin; jb < jend; jb += 64) {
+    const int j = jb + lane;
+    float acc[kRowsPerWave] = {0.f, 0.f, 0.f, 0.f};
+    if (j < jend) {
+      const float4* kr = reinterpret_cast<const float4*>(k_sum + ((size_t)j * Hkv + g) * D);
+#pragma unroll 4
+      for (int x = 0; x < D / 4; ++x) {
+        const float4 kv = kr[x];
+#pragma unroll
+        for (int r = 0; r < kRowsPerWave; ++r) {
+          const float4 qv = *reinterpret_cast<const float4*>(&qs[wave][r][4 * x]);
+          acc[r] = fmaf(qv.x, kv.x, acc[r]);
+          acc[r] = fmaf(qv.y, kv.y, acc[r]);
+          acc[r] = fmaf(qv.z, kv.z, acc[r]);
+          acc[r] = fmaf(qv.w, kv.w, acc[r]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r) {
+      if (!select[r] || jb >= i0 + r || jb + 64 <= first[r]) continue;   // wave-uniform
+      const bool ok = j >= first[r] && j < i0 + r;
+      const uint64_t key = ok ? rank_key(acc[r], j) : 0ull;
+      const uint64_t kth = shfl_u64(top[r], kk[r] - 1);
+      if (__ballot(key > kth) == 0ull) continue;
+      top[r] = merge_batch(top[r], key, lane);
+    }
+  }
+
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; ++r) {
+    const int i = i0 + r;
+    if (i >= C) continue;
+    int32_t* out = block_idx + (size_t)h * nnz + row_ptr[i];
+    if (select[r]) {
+      const uint32_t jj = lane < kk[r] ? (uint32_t)key_chunk(top[r]) : 0xFFFFFFFFu;
+      const uint32_t s = wave_sort_u32_asc(jj, lane);
+      if (lane < kk[r]) out[lane] = (int32_t)s;
+      if (lane == 0) out[kk[r]] = i;
+    } else if (kk[r] >= nc[r]) {             // every earlier chunk is kept
+      for (int x = lane; x < nc[r]; x += 64) out[x] = first[r] + x;
+      if (lane == 0) out[nc[r]] = i;
+    } else if (kk[r] == 0) {
+      if (lane == 0) out[0] = i;
+    }
+    // otherwise 64 < kk < nc: the general kernel writes this row
+  }
+}
+
+// General rows: more than 64 kept chunks out of a longer candidate list.
+template <int D>
+__global__ __launch_bounds__(kWideThreads) void route_wide_kernel(
+    const float* __restrict__ q_sum, const float* __restrict__ k_sum,
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ seq_chunk_start,
+    int32_t* __restrict__ block_idx, int B, int C, int Hq, int Hkv, long long nnz) {
+  __shared__ uint64_t keys[kMaxCand];
+  __shared__ uint32_t flags[kMaxCand / 32];
+  __shared__ float qrow[D];
+  __shared__ int warp_total[kWideThreads / 64];
+  const int i = blockIdx.x;
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int first = seq_chunk_start[seq_of_chunk(seq_chunk_start, B, i)];
+  const int n = i - first;
+  const int kk = row_ptr[i + 1] - row_ptr[i] - 1;
+  if (!(kk > kMaxTop && kk < n)) return;     // block-uniform
+  const int g = h / (Hq / Hkv);
+  int npad = 1;
+  while (npad < n) npad <<= 1;
+
+  for (int x = tid; x < D; x += kWideThreads) qrow[x] = q_sum[((size_t)i * Hq + h) * D + x];
+  for (int x = tid; x < kMaxCand / 32; x += kWideThreads) flags[x] = 0u;
+  __syncthreads();
+  for (int x = tid; x < npad; x += kWideThreads) {
+    uint64_t key = 0ull;
+    if (x < n) {
+      const int j = first + x;
+      const float* kr = k_sum + ((size_t)j * Hkv + g) * D;
+      float acc = 0.f;
+      for (int y = 0; y < D; ++y) acc = fmaf(qrow[y], kr[y], acc);
+      key = rank_key(acc, j);
+    }
+    keys[x] = key;
+  }
+  __syncthreads();
+  for (int size = 2; size <= npad; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int p = tid; p < npad / 2; p += kWideThreads) {
+        const int a = 2 * stride * (p / stride) + (p % stride);
+        const int b = a + stride;
+        const bool desc = (a & size) == 0;
+        const uint64_t ka = keys[a], kb = keys[b];
+        if ((ka < kb) == desc) { keys[a] = kb; keys[b] = ka; }
+      }
+      __syncthreads();
+    }
+  }
+  for (int x = tid; x < kk; x += kWideThreads) {
+    const int loc = key_chunk(keys[x]) - first;
+    atomicOr(&flags[loc >> 5], 1u << (loc & 31));
+  }
+  __syncthreads();
+  // Ascending compaction of the flagged chunks: each wave counts a quarter, then writes.
+  int32_t* out = block_idx + (size_t)h * nnz + row_ptr[i];
+  const int wave = tid >> 6, lane = tid & 63;
+  const int per = (n + 4 * 64 - 1) / (4 * 64) * 64;
+  const int lo = wave * per, hi = min(n, lo + per);
+  int cnt = 0;
+  for (int base = lo; base < hi; base += 64) {
+    const int x = base + lane;
+    const bool f = x < hi && ((flags[x >> 5] >> (x & 31)) & 1u);
+    cnt += __popcll(__ballot(f));
+  }
+  if (lane == 0) warp_total[wave] = cnt;
+  __syncthreads();
+  int pos = 0;
+  for (int w = 0; w < wave; ++w) pos += warp_total[w];
+  for (int base = lo; base < hi; base += 64) {
+    const int x = base + lane;
+    const bool f = x < hi && ((flags[x >> 5] >> (x & 31)) & 1u);
+    const uint64_t bal = __ballot(f);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (f) out[pos + before] = first + x;
+    pos += __popcll(bal);
+  }
+  if (tid == 0) out[kk] = i;
+}
+
+template <int D>
+hipError_t launch_route_d(const Plan& p, const float* q_sum, const float* k_sum, const int32_t* row_ptr,
+                          int64_t nnz, int32_t* block_idx, bool wide_rows, hipStream_t stream) {
+  dim3 grid((p.C + kRowsPerWave - 1) / kRowsPerWave, (p.Hq + kWaves - 1) / kWaves);
+  hipLaunchKernelGGL(route_kernel<D>, grid, dim3(kWaves * 64), 0, stream, q_sum, k_sum, row_ptr,
+                     p.seq_chunk_start, block_idx, p.B, p.C, p.Hq, p.Hkv, (long long)nnz);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || !wide_rows) return err;
+  hipLaunchKernelGGL(route_wide_kernel<D>, dim3(p.C, p.Hq), dim3(kWideThreads), 0, stream, q_sum, k_sum,
+                     row_ptr, p.seq_chunk_start, block_idx, p.B, p.C, p.Hq, p.Hkv, (long long)nnz);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_route(const Plan& p, const float* q_sum, const float* k_sum, const int32_t* row_ptr,
+                        int64_t nnz, int32_t* block_idx, bool wide_rows, hipStream_t stream) {
+  if (p.C == 0) return hipSuccess;
+  switch (p.d) {
+    case 32: return launch_route_d<32>(p, q_sum, k_sum, row_ptr, nnz, block_idx, wide_rows, stream);
+    case 64: return launch_route_d<64>(p, q_sum, k_sum, row_ptr, nnz, block_idx, wide_rows, stream);
+    case 128: return launch_route_d<128>(p, q_sum, k_sum, row_ptr, nnz, block_idx, wide_rows, stream);
+    case 256: return launch_route_d<256>(p, q_sum, k_sum, row_ptr, nnz, block_idx, wide_rows, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dhsa

@@ -1,0 +1,150 @@
+/*
+ * dhsa.h - C ABI of the MI355X (gfx950) DHSA chunk-routed sparse causal prefill.
+ *
+ * Dynamic Hierarchical Sparse Attention splits each sequence into
+ * variable-length chunks, represents every chunk by the average of its token
+ * vectors scaled by the square root of the chunk size, scores chunk pairs
+ * causally, upsamples the chunk scores to token level and runs exact softmax
+ * attention over the token interactions that survive ("Long-Context Modeling
+ * with Dynamic Hierarchical Sparse Attention for On-Device LLMs", Abstract and
+ * Innovation; "... for Memory-Constrained LLM Inference", ICML 2026 spotlight
+ * page, Abstract).  The pages leave the chunk rule, the keep budget and the
+ * diagonal open; here they are explicit: boundaries are an input, each query
+ * chunk keeps its top-k earlier key chunks plus itself, ties go to the lower
+ * chunk index.  Because the budget is counted in chunks, the token-level
+ * importance obtained by broadcasting chunk scores keeps exactly the union of
+ * the kept chunks' tokens (causally masked), so routing is decided per chunk.
+ *
+ * Conventions shared by every call
+ *  - Layout "THD": tokens of all sequences packed back to back.
+ *      q   [T, Hq,  d]   k, v [T, Hkv, d]   out [T, Hq, d]   (row-major, contiguous)
+ *      q_sum [C, Hq, d], k_sum [C, Hkv, d]  float32
+ *    q/k/v/out are float32 (DHSA_F32) or bfloat16 (DHSA_BF16).  Base pointers
+ *    must be 16-byte aligned.
+ *  - GQA: query head h reads KV head h / (Hq / Hkv); Hq % Hkv == 0.
+ *  - Chunk ids are global (0..C-1); the chunks of sequence b are
+ *    seq_chunk_start[b] .. seq_chunk_start[b+1]-1 and tile its tokens exactly.
+ *  - Pointers without the h_ prefix are HIP device memory; h_ pointers are
+ *    host memory.  Everything is OWNED BY THE CALLER: the library allocates
+ *    no device memory, keeps no mutable global state, never synchronises, and
+ *    enqueues its kernels on `stream` (a hipStream_t; NULL = default stream).
+ *  - Errors: every argument, shape and layout problem is detected on the host
+ *    (from the h_ mirrors) and returned BEFORE anything is launched; outputs
+ *    are then untouched.  A failed launch returns DHSA_ERR_LAUNCH.  The device
+ *    arrays must hold the same values as their host mirrors; if they do not,
+ *    behaviour is undefined.
+ *  - Supported: DHSA_BF16 with d in {64, 128, 256}; DHSA_F32 with d in
+ *    {32, 64, 128}.  At most DHSA_MAX_CHUNKS_PER_SEQ chunks per sequence.
+ *  - Empty batches (T == 0 or C == 0) are valid and launch nothing.
+ */
+#ifndef DHSA_H
+#define DHSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DHSA_ABI_VERSION 1
+#define DHSA_MAX_CHUNKS_PER_SEQ 8192
+
+typedef enum dhsa_status {
+  DHSA_OK = 0,
+  DHSA_ERR_NULL_ARG = 1,     /* a required pointer is NULL                          */
+  DHSA_ERR_BAD_SHAPE = 2,    /* negative sizes, Hq % Hkv != 0, nnz mismatch          */
+  DHSA_ERR_BAD_LAYOUT = 3,   /* offsets not monotone, empty chunk, chunk crosses seq */
+  DHSA_ERR_BAD_BUDGET = 4,   /* negative top-k                                       */
+  DHSA_ERR_UNSUPPORTED = 5,  /* dtype / head_dim / chunk count outside the support   */
+  DHSA_ERR_LAUNCH = 6        /* hipGetLastError after a launch was not hipSuccess    */
+} dhsa_status;
+
+typedef enum dhsa_dtype { DHSA_F32 = 0, DHSA_BF16 = 1 } dhsa_dtype;
+
+/* Packed varlen batch description.  Device arrays feed the kernels; the host
+ * mirrors (required, same contents) are used for validation and launch
+ * sizing. */
+typedef struct dhsa_layout {
+  int32_t num_seqs;                  /* B >= 0                                   */
+  int32_t total_tokens;              /* T = cu_seqlens[B]                        */
+  int32_t total_chunks;              /* C = seq_chunk_start[B]                   */
+  int32_t num_q_heads;               /* Hq >= 1                                  */
+  int32_t num_kv_heads;              /* Hkv >= 1, Hq % Hkv == 0                  */
+  int32_t head_dim;                  /* d                                        */
+  int32_t dtype;                     /* dhsa_dtype of q, k, v, out               */
+  const int32_t* cu_seqlens;         /* device [B+1] token offsets, [0] = 0      */
+  const int32_t* cu_chunks;          /* device [C+1] global chunk starts, [C]=T  */
+  const int32_t* seq_chunk_start;    /* device [B+1] first chunk of each seq     */
+  const int32_t* h_cu_seqlens;       /* host mirror of cu_seqlens                */
+  const int32_t* h_cu_chunks;        /* host mirror of cu_chunks                 */
+  const int32_t* h_seq_chunk_start;  /* host mirror of seq_chunk_start           */
+} dhsa_layout;
+
+/* ABI version (DHSA_ABI_VERSION). */
+int32_t dhsa_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* dhsa_status_str(int32_t status);
+
+/* Host-only check of a layout (the same check every call below performs):
+ * offsets start at 0 and are monotone, every chunk has >= 1 token, the chunks
+ * of each sequence tile its token range, and the shape fields are supported. */
+dhsa_status dhsa_validate_layout(const dhsa_layout* layout);
+
+/* Routing plan (host only, pure).  Row i of the compressed block list keeps
+ * min(h_topk[i], i_loc) + 1 key chunks, i_loc = i - first chunk of i's
+ * sequence: the top-k earlier chunks plus the diagonal.
+ *   h_topk     host [C]   off-diagonal key-chunk budget per query chunk (>= 0)
+ *   h_row_ptr  host [C+1] written: CSR row offsets, shared by all q heads
+ *   nnz        written: h_row_ptr[C], the entries per q head */
+dhsa_status dhsa_route_plan(const dhsa_layout* layout, const int32_t* h_topk,
+                            int32_t* h_row_ptr, int64_t* nnz);
+
+/* Stage 1: length-normalised chunk summaries ("Long-Context Modeling with
+ * Dynamic Hierarchical Sparse Attention for On-Device LLMs", Abstract and
+ * Innovation: the average of the chunk's token vectors times
+ * sqrt(chunk size)), for Q and K:
+ *   q_sum[c, h, :] = (sum_{t in chunk c} q[t, h, :]) / sqrt(n_c),
+ *   k_sum[c, g, :] likewise from k.
+ * fp32 accumulation.  q_sum and k_sum are written completely. */
+dhsa_status dhsa_chunk_summarize(const dhsa_layout* layout, const void* q, const void* k,
+                                 float* q_sum, float* k_sum, void* stream);
+
+/* Stage 2: causal chunk routing (same page, Abstract: chunk-level similarity
+ * upsampled to token level decides the kept interactions; ICML 2026 page,
+ * Abstract: routing is causal).  For q head h and query chunk i, every earlier
+ * chunk j of the same sequence is scored s_j = q_sum[i, h, :] . k_sum[j, h/G, :]
+ * (fp32); the top (row length - 1) by (s_j descending, j ascending) are kept,
+ * then i itself.  Row (h, i) is written to
+ *   block_idx[h * nnz + row_ptr[i] .. h * nnz + row_ptr[i+1] - 1]
+ * in ascending chunk order (so the diagonal is last).
+ *   row_ptr    device [C+1] from dhsa_route_plan (its host copy h_row_ptr is
+ *              used for validation)
+ *   block_idx  device [Hq, nnz] int32, written completely */
+dhsa_status dhsa_route(const dhsa_layout* layout, const float* q_sum, const float* k_sum,
+                       const int32_t* row_ptr, const int32_t* h_row_ptr, int64_t nnz,
+                       int32_t* block_idx, void* stream);
+
+/* Stage 3: block-sparse causal prefill (ICML 2026 page, Abstract: tiled
+ * backend; exact softmax over the kept token interactions).  Query token t of
+ * chunk i, head h attends to every key u <= t lying in a kept chunk of row
+ * (h, i):
+ *   out[t, h, :] = sum_u softmax_u(softmax_scale * q[t,h,:] . k[u,g,:]) v[u,g,:]
+ *   lse[h, t]    = log sum_u exp(softmax_scale * q[t,h,:] . k[u,g,:])   (natural log)
+ * fp32 accumulation; out is rounded to its dtype (bf16: to nearest even).
+ *   row_ptr, block_idx  device CSR as written by dhsa_route (or any list in the
+ *              same format: ascending, inside the query chunk's sequence, j <= i,
+ *              with the diagonal present)
+ *   lse        device [Hq, T] float32 or NULL
+ * out (and lse) are written completely. */
+dhsa_status dhsa_sparse_prefill(const dhsa_layout* layout, const void* q, const void* k,
+                                const void* v, const int32_t* row_ptr, const int32_t* h_row_ptr,
+                                int64_t nnz, const int32_t* block_idx, float softmax_scale,
+                                void* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DHSA_H */

@@ -1,0 +1,145 @@
+"""CPU tests of the C ABI: the library loads, exports every declared entry point, and
+rejects bad arguments on the host before anything would be launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from dynamic_sparse_attention_dhsa_amd import binding as Bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dhsa.h")
+
+OK, NULL, SHAPE, LAYOUT, BUDGET, UNSUP = 0, 1, 2, 3, 4, 5
+FAKE = 0x1000   # stands in for device pointers: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(dhsa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_three_stages():
+    names = declared_functions()
+    for n in ("dhsa_chunk_summarize", "dhsa_route", "dhsa_sparse_prefill", "dhsa_route_plan"):
+        assert n in names
+    assert set(names) == set(Bd.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = Bd.load_library()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert lib.dhsa_abi_version() == 1
+    assert lib.dhsa_status_str(5).decode().startswith("DHSA_ERR_UNSUPPORTED")
+
+
+class Mirror:
+    def __init__(self, cs, cc, sc, Hq=4, Hkv=2, d=128, dtype=1, T=None, C=None, B=None):
+        self.cs, self.cc, self.sc = (np.ascontiguousarray(x, np.int32) for x in (cs, cc, sc))
+        B = len(cs) - 1 if B is None else B
+        T = int(self.cs[-1]) if T is None else T
+        C = len(cc) - 1 if C is None else C
+        self.s = Bd.LayoutStruct(B, T, C, Hq, Hkv, d, dtype, FAKE, FAKE, FAKE, self.cs.ctypes.data,
+                                 self.cc.ctypes.data, self.sc.ctypes.data)
+
+    def ref(self):
+        return ctypes.byref(self.s)
+
+
+GOOD = ([0, 10, 17], [0, 4, 10, 13, 17], [0, 2, 4])
+
+
+def test_validate_good_and_bad_layouts():
+    lib = Bd.load_library()
+    assert lib.dhsa_validate_layout(Mirror(*GOOD).ref()) == OK
+    assert lib.dhsa_validate_layout(None) == NULL
+    bad = {
+        "chunk crosses sequence": ([0, 10, 17], [0, 4, 11, 13, 17], [0, 2, 4]),
+        "empty chunk": ([0, 10, 17], [0, 4, 4, 10, 17], [0, 3, 4]),
+        "not starting at zero": ([0, 10, 17], [1, 4, 10, 13, 17], [0, 2, 4]),
+        "seq start out of order": ([0, 10, 17], [0, 4, 10, 13, 17], [0, 5, 4]),
+        "tokens not covered": ([0, 10, 18], [0, 4, 10, 13, 17], [0, 2, 4]),
+    }
+    for name, lay in bad.items():
+        assert lib.dhsa_validate_layout(Mirror(*lay).ref()) in (LAYOUT,), name
+    assert lib.dhsa_validate_layout(Mirror(*GOOD, Hq=6, Hkv=4).ref()) == SHAPE
+    assert lib.dhsa_validate_layout(Mirror(*GOOD, d=96).ref()) == UNSUP
+    assert lib.dhsa_validate_layout(Mirror(*GOOD, dtype=7).ref()) == UNSUP
+    assert lib.dhsa_validate_layout(Mirror(*GOOD, dtype=0, d=256).ref()) == UNSUP
+    m = Mirror(*GOOD)
+    m.s.h_cu_chunks = None
+    assert lib.dhsa_validate_layout(m.ref()) == NULL
+    m = Mirror(*GOOD)
+    m.s.cu_chunks = None
+    assert lib.dhsa_validate_layout(m.ref()) == NULL
+
+
+def test_empty_batch_is_valid_and_launches_nothing():
+    lib = Bd.load_library()
+    m = Mirror([0], [0], [0], B=0, T=0, C=0)
+    assert lib.dhsa_validate_layout(m.ref()) == OK
+    rp = np.zeros(1, np.int32)
+    nnz = ctypes.c_int64(-1)
+    tk = np.zeros(1, np.int32)
+    assert lib.dhsa_route_plan(m.ref(), tk.ctypes.data, rp.ctypes.data, ctypes.byref(nnz)) == OK and nnz.value == 0
+    # empty sequences inside a batch are valid too
+    assert lib.dhsa_validate_layout(Mirror([0, 0, 5, 5], [0, 2, 5], [0, 0, 2, 2]).ref()) == OK
+    # with C == 0 the stage calls return before touching any pointer
+    assert lib.dhsa_chunk_summarize(m.ref(), None, None, None, None, None) == OK
+    assert lib.dhsa_route(m.ref(), None, None, None, rp.ctypes.data, 0, None, None) == OK
+    assert lib.dhsa_sparse_prefill(m.ref(), None, None, None, None, rp.ctypes.data, 0, None, 0.1, None, None,
+                                   None) == OK
+
+
+def test_route_plan_matches_budget_rule():
+    lib = Bd.load_library()
+    m = Mirror(*GOOD)
+    tk = np.array([3, 0, 1, 5], np.int32)
+    rp = np.zeros(5, np.int32)
+    nnz = ctypes.c_int64()
+    assert lib.dhsa_route_plan(m.ref(), tk.ctypes.data, rp.ctypes.data, ctypes.byref(nnz)) == OK
+    # seq 0: chunks 0,1 (i_loc 0,1) -> 1, 1 ; seq 1: chunks 2,3 (i_loc 0,1) -> 1, 2
+    assert rp.tolist() == [0, 1, 2, 3, 5] and nnz.value == 5
+    tk[2] = -1
+    assert lib.dhsa_route_plan(m.ref(), tk.ctypes.data, rp.ctypes.data, ctypes.byref(nnz)) == BUDGET
+    assert lib.dhsa_route_plan(m.ref(), None, rp.ctypes.data, ctypes.byref(nnz)) == NULL
+
+
+def test_stage_calls_reject_before_launch():
+    lib = Bd.load_library()
+    m = Mirror(*GOOD)
+    rp = np.array([0, 1, 2, 3, 5], np.int32)
+    assert lib.dhsa_chunk_summarize(m.ref(), None, FAKE, FAKE, FAKE, None) == NULL
+    bad = Mirror(*GOOD, d=80)
+    assert lib.dhsa_chunk_summarize(bad.ref(), FAKE, FAKE, FAKE, FAKE, None) == UNSUP
+    # row pointers inconsistent with nnz or with the layout
+    assert lib.dhsa_route(m.ref(), FAKE, FAKE, FAKE, rp.ctypes.data, 6, FAKE, None) == SHAPE
+    rp_bad = np.array([0, 2, 3, 4, 6], np.int32)      # row 0 has i_loc 0 but 2 entries
+    assert lib.dhsa_route(m.ref(), FAKE, FAKE, FAKE, rp_bad.ctypes.data, 6, FAKE, None) == SHAPE
+    assert lib.dhsa_route(m.ref(), FAKE, FAKE, FAKE, None, 5, FAKE, None) == NULL
+    assert lib.dhsa_route(m.ref(), None, FAKE, FAKE, rp.ctypes.data, 5, FAKE, None) == NULL
+    # scale must be positive and finite
+    for s in (0.0, -1.0, float("inf"), float("nan")):
+        assert lib.dhsa_sparse_prefill(m.ref(), FAKE, FAKE, FAKE, FAKE, rp.ctypes.data, 5, FAKE, s, FAKE, None,
+                                       None) == SHAPE
+    assert lib.dhsa_sparse_prefill(m.ref(), FAKE, FAKE, None, FAKE, rp.ctypes.data, 5, FAKE, 0.1, FAKE, None,
+                                   None) == NULL
+
+
+def test_too_many_chunks_per_sequence_is_unsupported():
+    lib = Bd.load_library()
+    n = 8193
+    cc = np.arange(n + 1, dtype=np.int32)
+    m = Mirror([0, n], cc, [0, n])
+    assert lib.dhsa_validate_layout(m.ref()) == UNSUP
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    lay = Bd.Layout.__new__(Bd.Layout)
+    lay.dtype, lay.total_tokens, lay.head_dim = torch.bfloat16, 4, 64
+    with pytest.raises(Bd.DhsaError):
+        lay._check_tensor(torch.zeros(4, 1, 64, dtype=torch.bfloat16), 1, "q")
