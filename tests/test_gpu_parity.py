@@ -108,6 +108,11 @@ def check_routing(case: Case, q_sum=None, k_sum=None, heads=None):
 def check_attention(case: Case, heads=None, chunks=None):
     """GPU attention and oracle attention on the oracle's block list, on the requested rows."""
     g_o, g_l = case.gpu_attend(case.o_bidx)
+    # the output does not depend on whether the LSE is requested
+    bidx = torch.from_numpy(np.ascontiguousarray(case.o_bidx)).cuda()
+    g_o2 = D.sparse_prefill(case.layout, case.plan, case.q, case.k, case.v, bidx, case.w.softmax_scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(g_o2.float().cpu().numpy(), g_o)
     o_o, o_l = case.oracle_attend(case.o_bidx, heads, chunks)
     sel = ~np.isnan(o_o)
     assert sel.any()
