@@ -50,11 +50,10 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef s16x4 __attribute__((address_space(3))) lds_s16x4;
 
 #ifndef DHSA_VPAD
-#define DHSA_VPAD 16
+#define DHSA_VPAD 32
 #endif
 
 constexpr int kMaxWords = DHSA_MAX_WORDS;      // bitmap words per head (32 chunks each)
-constexpr int kMaxHP = 8;                      // heads per workgroup at most
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleLog2 = 8.0f;           // move the running max only past 2^8
 constexpr int kBufWord3 = 0x00020000;          // gfx9 buffer resource: raw 32-bit data
@@ -64,15 +63,14 @@ constexpr int kSgVALU = 0x002, kSgMFMA = 0x008, kSgVMEM = 0x020, kSgDSR = 0x100,
 
 template <int D>
 struct Geo {
-  static constexpr int NW = (D >= 256) ? 4 : 8;          // waves per workgroup
+  static constexpr int NW = 4;                           // waves per workgroup (two workgroups per CU)
   static constexpr int NT = NW * 64;
   static constexpr int BK = 64;                          // keys per tile (two 32-key blocks)
   static constexpr int GR = D / 8;                       // 16-byte granules per row
   static constexpr int KS = D + 8;                       // K row stride in LDS (bf16)
   static constexpr int VS = D + DHSA_VPAD;               // V row stride in LDS (bf16)
   static constexpr int KTILE = BK * KS;
-  static constexpr int STAGE = BK * (KS + VS);
-  static constexpr int NSTAGE = (D >= 256) ? 2 : 3;
+  static constexpr int VTILE = BK * VS;
   static constexpr int LOADS = BK * GR / NT;             // granules per thread per tensor per tile
   static constexpr int DSTEPS = D / 16;
   static constexpr int DBLK = D / 32;
@@ -127,8 +125,11 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
     long long nnz, float scale, int hp, int head_slots, int row_tiles) {
   using GE = Geo<D>;
   constexpr int NW = GE::NW, NT = GE::NT, BK = GE::BK;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[GE::NSTAGE * GE::STAGE];
-  __shared__ uint32_t bm[kMaxHP][kMaxWords];
+  // two-stage rings: K of the tile after next and V of the next tile are written while the
+  // current tile is computed, so one barrier per tile suffices
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2 * GE::KTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2 * GE::VTILE];
+  __shared__ uint32_t bm[GE::NW][kMaxWords];
 
   // ---- block -> (KV head, chunk, head slot, row tile); one XCD per (KV head, chunk)
   const int G = Hq / Hkv;
@@ -209,35 +210,41 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
   // ---- staging: buffer loads -> registers -> LDS (K and V both stored as rows, padded)
   auto voff = [&](int m) { const int idx = tid + m * NT; return ((idx / GE::GR) * Hkv * D + (idx % GE::GR) * 8) * 2; };
   auto lds_k = [&](int m) { const int idx = tid + m * NT; return (idx / GE::GR) * GE::KS + (idx % GE::GR) * 8; };
-  auto lds_v = [&](int m) { const int idx = tid + m * NT; return GE::KTILE + (idx / GE::GR) * GE::VS + (idx % GE::GR) * 8; };
-  uint4 kreg[GE::LOADS], vreg[GE::LOADS];
-  auto load_tile = [&](const TileRef& t) {
-    // byte range of this KV head's rows from the tile start to the last token
+  auto lds_v = [&](int m) { const int idx = tid + m * NT; return (idx / GE::GR) * GE::VS + (idx % GE::GR) * 8; };
+  // buffer range: this KV head's rows from the tile start to the last token (nothing past T is read)
+  auto tile_rsrc = [&](const uint16_t* base_ptr, const TileRef& t) {
     const long long rows_left = (long long)(T - t.kt) * Hkv - gk;
     const long long cap = (long long)BK * Hkv * D * 2;
     const int nbytes = (int)min(rows_left * D * 2, cap);
-    const size_t base = ((size_t)t.kt * Hkv + gk) * D;
-    __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + base), (short)0, nbytes, kBufWord3);
-    __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + base), (short)0, nbytes, kBufWord3);
-#pragma unroll
-    for (int m = 0; m < GE::LOADS; ++m) {
-      kreg[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, voff(m), 0, 0));
-      vreg[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff(m), 0, 0));
-    }
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base_ptr + ((size_t)t.kt * Hkv + gk) * D), (short)0, nbytes,
+                                             kBufWord3);
   };
-  auto store_tile = [&](int stage) {
-    uint16_t* base = lds + stage * GE::STAGE;
+  uint4 kreg[GE::LOADS], vreg[GE::LOADS];
+  auto load_k = [&](const TileRef& t) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(k, t);
 #pragma unroll
-    for (int m = 0; m < GE::LOADS; ++m) {
-      *reinterpret_cast<uint4*>(base + lds_k(m)) = kreg[m];
-      *reinterpret_cast<uint4*>(base + lds_v(m)) = vreg[m];
-    }
+    for (int m = 0; m < GE::LOADS; ++m)
+      kreg[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff(m), 0, 0));
+  };
+  auto load_v = [&](const TileRef& t) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(v, t);
+#pragma unroll
+    for (int m = 0; m < GE::LOADS; ++m)
+      vreg[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff(m), 0, 0));
+  };
+  auto store_k = [&](int stage) {
+#pragma unroll
+    for (int m = 0; m < GE::LOADS; ++m) *reinterpret_cast<uint4*>(k_lds + stage * GE::KTILE + lds_k(m)) = kreg[m];
+  };
+  auto store_v = [&](int stage) {
+#pragma unroll
+    for (int m = 0; m < GE::LOADS; ++m) *reinterpret_cast<uint4*>(v_lds + stage * GE::VTILE + lds_v(m)) = vreg[m];
   };
 
   // ---- per-lane LDS read bases
   const int k_lane = col * GE::KS + half * 8;               // K row 32b + col, dims 16s + 8*half
   const int grp = (lane >> 4) & 3, ii = lane & 15;          // transpose load: 4-key x 16-dim block per 16 lanes
-  const int v_lane = GE::KTILE + (4 * (grp >> 1) + (ii >> 2)) * GE::VS + 16 * (grp & 1) + 4 * (ii & 3);
+  const int v_lane = (4 * (grp >> 1) + (ii >> 2)) * GE::VS + 16 * (grp & 1) + 4 * (ii & 3);
 
   f32x16 o[GE::DBLK];
 #pragma unroll
@@ -271,7 +278,7 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
   uint32_t pw[16];
   auto region_a = [&](auto qn_c, auto cb_c, int stage_n, f32x16 (&sn)[2], f32x16 (&sc)[2], float& alpha) {
     constexpr int QN = decltype(qn_c)::value, CB = decltype(cb_c)::value;
-    const uint16_t* kb0 = lds + stage_n * GE::STAGE + k_lane;
+    const uint16_t* kb0 = k_lds + stage_n * GE::KTILE + k_lane;
 #pragma unroll
     for (int st = 0; st < GE::DSTEPS; ++st) {
       if constexpr (QN >= 1) {
@@ -284,12 +291,16 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
       }
     }
     if constexpr (CB >= 1) {
-      float mx = -INFINITY;
+      // reductions as shallow trees (four independent partial results) to keep dependency chains short
+      float m4[4];
 #pragma unroll
-      for (int b = 0; b < CB; ++b)
+      for (int x = 0; x < 4; ++x) m4[x] = fmaxf(fmaxf(sc[0][x], sc[0][x + 4]), fmaxf(sc[0][x + 8], sc[0][x + 12]));
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[b][r]);
-      mx = max_halves(mx);
+      for (int b = 1; b < CB; ++b)
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          m4[x] = fmaxf(fmaxf(m4[x], sc[b][x]), fmaxf(fmaxf(sc[b][x + 4], sc[b][x + 8]), sc[b][x + 12]));
+      const float mx = max_halves(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
       const bool grow = mx > m_ref + grow_raw;
       const float m_new = grow ? mx : m_ref;
       alpha = grow ? __builtin_amdgcn_exp2f((m_ref - m_new) * c2) : 1.f;   // 0 at the first tile
@@ -299,22 +310,23 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
       for (int b = 0; b < CB; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sc[b][r] = __builtin_amdgcn_exp2f(fmaf(sc[b][r], c2, -mb));
-      float lb = 0.f;
+      float lb4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int b = 0; b < CB; ++b)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
           pw[b * 8 + r / 2] = pack_bf16(sc[b][r], sc[b][r + 1]);
-          lb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[b * 8 + r / 2]), ones, lb, false);
+          lb4[(r / 2) & 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[b * 8 + r / 2]), ones,
+                                                             lb4[(r / 2) & 3], false);
         }
-      lb_run = lb_run * alpha + sum_halves(lb);
+      lb_run = lb_run * alpha + sum_halves((lb4[0] + lb4[1]) + (lb4[2] + lb4[3]));
       if constexpr (WITH_LSE) {
-        float ls = 0.f;
+        float ls4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int b = 0; b < CB; ++b)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) ls += sc[b][r];
-        l_run = l_run * alpha + sum_halves(ls);
+          for (int r = 0; r < 16; ++r) ls4[r & 3] += sc[b][r];
+        l_run = l_run * alpha + sum_halves((ls4[0] + ls4[1]) + (ls4[2] + ls4[3]));
       }
     }
     // interleave: each QK MFMA followed by its next K read and a slice of the softmax
@@ -330,12 +342,10 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
   };
 
   // O^T += V^T P^T for the current tile (CB blocks), interleaved with staging the tile after next.
-  auto region_b = [&](auto cb_c, int stage_c, bool do_store, int stage_w, bool do_load, const TileRef& tl) {
+  auto region_b = [&](auto cb_c, int stage_c) {
     constexpr int CB = decltype(cb_c)::value;
-    if (do_store) store_tile(stage_w);
-    if (do_load) load_tile(tl);
     if constexpr (CB > 0) {
-      const uint16_t* vb = lds + stage_c * GE::STAGE + v_lane;
+      const uint16_t* vb = v_lds + stage_c * GE::VTILE + v_lane;
 #pragma unroll
       for (int ks = 0; ks < 2 * CB; ++ks) {
         const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pw[ks * 4], pw[ks * 4 + 1], pw[ks * 4 + 2],
@@ -364,22 +374,20 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
     else if (qn) region_a(ic<2>{}, ic<0>{}, stage_n, sn, sc, alpha);
     else if (cb) region_a(ic<0>{}, ic<2>{}, stage_n, sn, sc, alpha);
   };
-  auto run_b = [&](int cb, int stage_c, bool do_store, int stage_w, bool do_load, const TileRef& tl) {
-    if (cb) region_b(ic<2>{}, stage_c, do_store, stage_w, do_load, tl);
-    else region_b(ic<0>{}, stage_c, do_store, stage_w, do_load, tl);
+  auto run_b = [&](int cb, int stage_c) {
+    if (cb) region_b(ic<2>{}, stage_c);
   };
 
-  // ---- prologue: stages 0 and 1 hold tiles 0 and 1, registers hold tile 2 in flight
+  // ---- prologue: K ring holds tiles 0 and 1, V ring tile 0; registers hold K of tile 2 and V of tile 1
   TileRef t0;
   t0.jl = __builtin_amdgcn_readfirstlane(next_union(bm, hp, 0, nbits));
   t0.kt = 0; t0.kend = 0;
   if (t0.jl >= 0) chunk_span(t0);
   TileRef t1 = next_tile(t0);
   TileRef t2 = next_tile(t1);
-  if (t0.jl >= 0) { load_tile(t0); store_tile(0); }
-  if (GE::NSTAGE > 2 && t1.jl >= 0) { load_tile(t1); store_tile(1); }
-  if (GE::NSTAGE > 2 && t2.jl >= 0) load_tile(t2);
-  if (GE::NSTAGE == 2 && t1.jl >= 0) load_tile(t1);
+  if (t0.jl >= 0) { load_k(t0); load_v(t0); store_k(0); store_v(0); }
+  if (t1.jl >= 0) { load_k(t1); store_k(1); load_v(t1); }
+  if (t2.jl >= 0) load_k(t2);
   __syncthreads();
 
   f32x16 sA[2], sB[2];
@@ -389,14 +397,18 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
     float dummy;
     run_a(cb_cur, 0, 0, sA, sB, dummy);        // S^T of tile 0
   }
+  __syncthreads();                             // K stage 0 is rewritten by the first iteration
   int stage = 0;
   // one iteration: softmax + PV of t0 (S^T in sc), QK^T of t1 (into sn)
   auto step = [&](f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-    const int st1 = (stage + 1 == GE::NSTAGE) ? 0 : stage + 1;
-    int cb_nxt = 0;
-    if constexpr (GE::NSTAGE > 2) {
-      cb_nxt = (t1.jl >= 0) ? busy : 0;
-    }
+    const int st1 = stage ^ 1;
+    // K(t2) -> K stage of t0 (read in the previous iteration), V(t1) -> V stage st1 (free since then)
+    const TileRef t3 = next_tile(t2);
+    if (t2.jl >= 0) store_k(stage);
+    if (t1.jl >= 0) store_v(st1);
+    if (t3.jl >= 0) load_k(t3);
+    if (t2.jl >= 0) load_v(t2);
+    const int cb_nxt = (t1.jl >= 0) ? busy : 0;
     if (cb_cur > 0 && needs_mask(t0)) apply_mask(sc, t0);
     float alpha = 1.f;
     run_a(cb_nxt, cb_cur, st1, sn, sc, alpha);
@@ -406,25 +418,9 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
     }
-    if constexpr (GE::NSTAGE > 2) {
-      const int st2 = (st1 + 1 == GE::NSTAGE) ? 0 : st1 + 1;
-      const TileRef t3 = next_tile(t2);
-      run_b(cb_cur, stage, t2.jl >= 0, st2, t3.jl >= 0, t3);
-      __syncthreads();
-      t0 = t1; t1 = t2; t2 = t3;
-    } else {
-      // two stages: the next tile is stored only after everyone is done with the current one
-      run_b(cb_cur, stage, false, 0, false, t1);
-      __syncthreads();
-      const TileRef t2n = next_tile(t1);
-      if (t1.jl >= 0) store_tile(st1);
-      if (t2n.jl >= 0) load_tile(t2n);
-      __syncthreads();
-      cb_nxt = (t1.jl >= 0) ? busy : 0;
-      float dummy;
-      run_a(cb_nxt, 0, st1, sn, sc, dummy);
-      t0 = t1; t1 = t2n;
-    }
+    run_b(cb_cur, stage);
+    __syncthreads();
+    t0 = t1; t1 = t2; t2 = t3;
     cb_cur = cb_nxt;
     stage = st1;
   };
@@ -460,7 +456,7 @@ hipError_t launch_d(const Plan& p, const void* q, const void* k, const void* v, 
   using GE = Geo<D>;
   const int G = p.Hq / p.Hkv;
   int hp = 1;
-  while (hp < GE::NW && hp < kMaxHP && G % (hp * 2) == 0) hp *= 2;
+  while (hp < GE::NW && G % (hp * 2) == 0) hp *= 2;
   const int rows_per_block = (GE::NW / hp) * 32;
   const int row_tiles = (p.max_chunk_len + rows_per_block - 1) / rows_per_block;
   const int head_slots = G / hp;
