@@ -197,13 +197,13 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
   };
   // (every field goes through readfirstlane: the walk is wave-uniform, and scalar registers keep the
   // buffer descriptors and branches built from it scalar)
-  auto chunk_span = [&](TileRef& t) {
+  auto chunk_span = [&](TileRef& t) __attribute__((always_inline)) {
     const int j = first + t.jl;
     t.kt = __builtin_amdgcn_readfirstlane(cu_chunks[j]);
     t.kend = __builtin_amdgcn_readfirstlane((j == i) ? diag_end : cu_chunks[j + 1]);
     t.keep = __builtin_amdgcn_readfirstlane((bm[hw][t.jl >> 5] >> (t.jl & 31)) & 1u);
   };
-  auto next_tile = [&](TileRef t) {
+  auto next_tile = [&](TileRef t) __attribute__((always_inline)) {
     if (t.jl < 0) return t;
     t.kt += BK;
     if (t.kt >= t.kend) {
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
   const int vv_lane = row_in * row_bytes + (slot ^ GE::vswz(row_in)) * 16;
   const int soff_wave = wave * GE::DPW * GE::RPD * row_bytes;
   // buffer range: this KV head's rows from the tile start to the last token (nothing past T is read)
-  auto tile_rsrc = [&](const uint16_t* base_ptr, const TileRef& t) {
+  auto tile_rsrc = [&](const uint16_t* base_ptr, const TileRef& t) __attribute__((always_inline)) {
     const int kt = __builtin_amdgcn_readfirstlane(t.kt);
     const long long rows_left = (long long)(T - kt) * Hkv - gk;
     const long long cap = (long long)BK * Hkv * D * 2;
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base_ptr + ((size_t)kt * Hkv + gk) * D), (short)0, nbytes,
                                              kBufWord3);
   };
-  auto load_k = [&](const TileRef& t, uint8_t* dst) {
+  auto load_k = [&](const TileRef& t, uint8_t* dst) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t r = tile_rsrc(k, t);
 #pragma unroll
     for (int m = 0; m < GE::DPW; ++m) {
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + (wave * GE::DPW + m) * 1024), 16, voff, soff, 0, 0);
     }
   };
-  auto load_v = [&](const TileRef& t, uint8_t* dst) {
+  auto load_v = [&](const TileRef& t, uint8_t* dst) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t r = tile_rsrc(v, t);
 #pragma unroll
     for (int m = 0; m < GE::DPW; ++m) {
@@ -283,10 +283,10 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
   // S^T[b][r] holds tile key 32b + 8(r/4) + 4*half + r%4 of query `col`
   // masking: tiles cut by the chunk end, tiles of chunks this head does not keep, and tiles of the
   // diagonal chunk with a key past the wave's first query row
-  auto needs_mask = [&](const TileRef& t) {
+  auto needs_mask = [&](const TileRef& t) __attribute__((always_inline)) {
     return t.kend - t.kt < BK || !t.keep || (first + t.jl == i && t.kt + BK - 1 > qr0);
   };
-  auto apply_mask = [&](f32x16 (&s)[2], const TileRef& t) {
+  auto apply_mask = [&](f32x16 (&s)[2], const TileRef& t) __attribute__((always_inline)) {
     int lim = t.kend - t.kt - 1;
     if (first + t.jl == i) lim = min(lim, tq - t.kt);
     if (!t.keep) lim = -1;
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
   // Leaves P^T of the current tile packed in pw and the running max / sums updated; returns alpha.
   uint32_t pw[16];
   auto region_a = [&](auto qn_c, auto sm_c, const uint8_t* kst, f32x16 (&sn)[2], f32x16 (&sc)[2],
-                      float& alpha) {
+                      float& alpha) __attribute__((always_inline)) {
     constexpr bool QN = decltype(qn_c)::value, SM = decltype(sm_c)::value;
     if constexpr (QN) {
       const uint8_t* kb = kst + 0;
@@ -366,7 +366,7 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
   };
 
   // O^T += V^T P^T for the current tile
-  auto region_b = [&](const uint8_t* vst) {
+  auto region_b = [&](const uint8_t* vst) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pw[ks * 4], pw[ks * 4 + 1], pw[ks * 4 + 2],
@@ -413,7 +413,7 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
 
   // One iteration with stage parity S: softmax and PV of t0 (S^T in sc, V in V stage S), QK^T of t1
   // (K in K stage 1 - S, into sn); meanwhile K of t2 lands in K stage S and V of t1 in V stage 1 - S.
-  auto step = [&](auto s_c, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+  auto step = [&](auto s_c, f32x16 (&sc)[2], f32x16 (&sn)[2]) __attribute__((always_inline)) {
     constexpr int S = decltype(s_c)::value;
     uint8_t* const k_fill = S ? k_st1 : k_st0;
     uint8_t* const k_read = S ? k_st0 : k_st1;
