@@ -54,9 +54,39 @@ def kept_flops(block_idx: np.ndarray, row_ptr: np.ndarray, cu_chunks: np.ndarray
 
 
 def stage_bytes(T, C, Hq, Hkv, d, s, nnz):
+    """Algorithmic bytes of stage 1 (Q, K read once, summaries written) and stage 2 (summaries read,
+    row pointers and per-chunk sequence starts read, block list written)."""
     b1 = T * (Hq + Hkv) * d * s + C * (Hq + Hkv) * d * 4
-    b2 = C * (Hq + Hkv) * d * 4 + (C + 1) * 4 + Hq * nnz * 4
+    b2 = C * (Hq + Hkv) * d * 4 + (C + 1) * 4 + C * 4 + Hq * nnz * 4
     return b1, b2
+
+
+def achievable_peaks(torch):
+    """Measured reference rates on this device: a large bf16 GEMM (hipBLASLt through torch) and a
+    1 GiB device-to-device copy.  Context for the roofline fractions, which use the published peaks."""
+    a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    x = torch.empty(512 * 1024 * 1024, device="cuda", dtype=torch.bfloat16)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.matmul(a, b)
+        y.copy_(x)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    e[0].record()
+    for _ in range(10):
+        torch.matmul(a, b)
+    e[1].record()
+    e[2].record()
+    for _ in range(10):
+        y.copy_(x)
+    e[3].record()
+    torch.cuda.synchronize()
+    t_mm = e[0].elapsed_time(e[1]) / 10 * 1e-3
+    t_cp = e[2].elapsed_time(e[3]) / 10 * 1e-3
+    del a, b, x, y
+    return {"bf16_gemm_8192_TFLOPs": 2 * 8192 ** 3 / t_mm / 1e12,
+            "copy_1GiB_GBps": 2 * 512 * 1024 * 1024 * 2 / t_cp / 1e9}
 
 
 def traffic_record(workload: str):
@@ -221,6 +251,11 @@ def main() -> int:
             "kept_density_vs_causal": F3 / (4.0 * d * causal_pairs),
         },
     }
+    peaks = achievable_peaks(torch)
+    result["roofline"]["achievable_peak_measured"] = peaks["bf16_gemm_8192_TFLOPs"]
+    result["roofline"]["frac_of_achievable"] = achieved / peaks["bf16_gemm_8192_TFLOPs"]
+    result["stages"]["copy_GBps_measured"] = peaks["copy_1GiB_GBps"]
+    result["stages"]["stages12_frac_of_copy"] = (b1 + b2) / (t1 + t2) / 1e9 / peaks["copy_1GiB_GBps"]
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, w.topk, args.cpu_budget)

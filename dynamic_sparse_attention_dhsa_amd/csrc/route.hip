@@ -14,9 +14,11 @@
 // the complemented chunk id), so a larger key is a better candidate and every
 // key is distinct: ties resolve to the lower chunk id exactly.
 //
-// Main kernel: a wave owns one q head and four consecutive query chunks.  It
-// walks the candidates in batches of 64 (one per lane), computes the four
-// rows' fp32 dot products, and keeps each row's best 64 keys as a sorted
+// Main kernel: a wave owns one q head and one query chunk (a workgroup: four q
+// heads of one chunk; chunks with the most candidates are launched first).  It
+// walks the candidates in batches of 64 (one per lane), computes the row's fp32
+// dot products (when the four heads share a KV head, each batch of K summaries
+// is staged once in LDS for all of them), and keeps the row's best 64 keys as a sorted
 // wave-wide list: a batch is bitonic-sorted across lanes, merged with the list
 // by an element-wise max against the reversed order, and re-sorted with a
 // bitonic half-cleaner cascade.  Batches that cannot beat the row's current
@@ -29,7 +31,6 @@ namespace dhsa {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kRowsPerWave = 4;
 constexpr int kMaxTop = 64;
 constexpr int kWideThreads = 256;
 constexpr int kMaxCand = 8192;
@@ -107,88 +108,84 @@ __global__ __launch_bounds__(kWaves * 64) void route_kernel(
     const float* __restrict__ q_sum, const float* __restrict__ k_sum,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ seq_chunk_start,
     int32_t* __restrict__ block_idx, int B, int C, int Hq, int Hkv, long long nnz) {
-  __shared__ float qs[kWaves][kRowsPerWave][D];
+  __shared__ float qs[kWaves][D];
+  __shared__ __attribute__((aligned(16))) float ks[64][D + 4];   // a batch of K summaries (padded rows)
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int h = blockIdx.y * kWaves + wave;
-  const int i0 = blockIdx.x * kRowsPerWave;
+  const int i = C - 1 - blockIdx.x;            // latest chunks (most candidates) first
   const int G = Hq / Hkv;
-  if (h >= Hq) return;                       // whole wave leaves; no block barrier below
+  // When the workgroup's four q heads share one KV head, each batch of K summaries is loaded once
+  // into LDS for all of them (block-uniform; then Hq % 4 == 0 and no wave leaves early).
+  const bool shared_kv = G % kWaves == 0;
+  if (h >= Hq) return;                         // only when Hq % 4 != 0: no block barrier is used then
   const int g = h / G;
 
-  int first[kRowsPerWave], kk[kRowsPerWave], nc[kRowsPerWave];
-  bool select[kRowsPerWave];
-  int jmin = 0x7fffffff, jend = 0;
-#pragma unroll
-  for (int r = 0; r < kRowsPerWave; ++r) {
-    const int i = i0 + r;
-    if (i < C) {
-      first[r] = seq_chunk_start[seq_of_chunk(seq_chunk_start, B, i)];
-      nc[r] = i - first[r];
-      kk[r] = row_ptr[i + 1] - row_ptr[i] - 1;
-      select[r] = kk[r] > 0 && kk[r] < nc[r] && kk[r] <= kMaxTop;
-      if (select[r]) { jmin = min(jmin, first[r]); jend = max(jend, i); }
-    } else {
-      first[r] = 0; nc[r] = 0; kk[r] = 0; select[r] = false;
-    }
-    for (int x = lane; x < D; x += 64)
-      qs[wave][r][x] = (i < C) ? q_sum[((size_t)i * Hq + h) * D + x] : 0.f;
-  }
+  const int first = seq_chunk_start[seq_of_chunk(seq_chunk_start, B, i)];
+  const int nc = i - first;
+  const int kk = row_ptr[i + 1] - row_ptr[i] - 1;
+  const bool select = kk > 0 && kk < nc && kk <= kMaxTop;   // same for every head of the chunk
+  for (int x = lane; x < D; x += 64) qs[wave][x] = q_sum[((size_t)i * Hq + h) * D + x];
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  uint64_t top[kRowsPerWave];
-#pragma unroll
-  for (int r = 0; r < kRowsPerWave; ++r) top[r] = 0;
-
-  for (int jb = jmin; jb < jend; jb += 64) {
-    const int j = jb + lane;
-    float acc[kRowsPerWave] = {0.f, 0.f, 0.f, 0.f};
-    if (j < jend) {
-      const float4* kr = reinterpret_cast<const float4*>(k_sum + ((size_t)j * Hkv + g) * D);
+  uint64_t top = 0;
+  if (select) {
+    for (int jb = first; jb < i; jb += 64) {
+      const int j = jb + lane;
+      float acc = 0.f;
+      if (shared_kv) {
+        __syncthreads();                       // the previous batch has been read
+        for (int x = threadIdx.x; x < 64 * (D / 4); x += kWaves * 64) {
+          const int row = x / (D / 4), c4 = x % (D / 4);
+          const int jj = jb + row;
+          const float4 kv = jj < i ? reinterpret_cast<const float4*>(k_sum + ((size_t)jj * Hkv + g) * D)[c4]
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+          *reinterpret_cast<float4*>(&ks[row][4 * c4]) = kv;
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int x = 0; x < D / 4; ++x) {
+          const float4 kv = *reinterpret_cast<const float4*>(&ks[lane][4 * x]);
+          const float4 qv = *reinterpret_cast<const float4*>(&qs[wave][4 * x]);
+          acc = fmaf(qv.x, kv.x, acc);
+          acc = fmaf(qv.y, kv.y, acc);
+          acc = fmaf(qv.z, kv.z, acc);
+          acc = fmaf(qv.w, kv.w, acc);
+        }
+      } else if (j < i) {
+        const float4* kr = reinterpret_cast<const float4*>(k_sum + ((size_t)j * Hkv + g) * D);
 #pragma unroll 4
-      for (int x = 0; x < D / 4; ++x) {
-        const float4 kv = kr[x];
-#pragma unroll
-        for (int r = 0; r < kRowsPerWave; ++r) {
-          const float4 qv = *reinterpret_cast<const float4*>(&qs[wave][r][4 * x]);
-          acc[r] = fmaf(qv.x, kv.x, acc[r]);
-          acc[r] = fmaf(qv.y, kv.y, acc[r]);
-          acc[r] = fmaf(qv.z, kv.z, acc[r]);
-          acc[r] = fmaf(qv.w, kv.w, acc[r]);
+        for (int x = 0; x < D / 4; ++x) {
+          const float4 kv = kr[x];
+          const float4 qv = *reinterpret_cast<const float4*>(&qs[wave][4 * x]);
+          acc = fmaf(qv.x, kv.x, acc);
+          acc = fmaf(qv.y, kv.y, acc);
+          acc = fmaf(qv.z, kv.z, acc);
+          acc = fmaf(qv.w, kv.w, acc);
         }
       }
-    }
-#pragma unroll
-    for (int r = 0; r < kRowsPerWave; ++r) {
-      if (!select[r] || jb >= i0 + r || jb + 64 <= first[r]) continue;   // wave-uniform
-      const bool ok = j >= first[r] && j < i0 + r;
-      const uint64_t key = ok ? rank_key(acc[r], j) : 0ull;
-      const uint64_t kth = shfl_u64(top[r], kk[r] - 1);
+      const uint64_t key = j < i ? rank_key(acc, j) : 0ull;
+      const uint64_t kth = shfl_u64(top, kk - 1);
       if (__ballot(key > kth) == 0ull) continue;
-      top[r] = merge_batch(top[r], key, lane);
+      top = merge_batch(top, key, lane);
     }
   }
 
-#pragma unroll
-  for (int r = 0; r < kRowsPerWave; ++r) {
-    const int i = i0 + r;
-    if (i >= C) continue;
-    int32_t* out = block_idx + (size_t)h * nnz + row_ptr[i];
-    if (select[r]) {
-      const uint32_t jj = lane < kk[r] ? (uint32_t)key_chunk(top[r]) : 0xFFFFFFFFu;
-      const uint32_t s = wave_sort_u32_asc(jj, lane);
-      if (lane < kk[r]) out[lane] = (int32_t)s;
-      if (lane == 0) out[kk[r]] = i;
-    } else if (kk[r] >= nc[r]) {             // every earlier chunk is kept
-      for (int x = lane; x < nc[r]; x += 64) out[x] = first[r] + x;
-      if (lane == 0) out[nc[r]] = i;
-    } else if (kk[r] == 0) {
-      if (lane == 0) out[0] = i;
-    }
-    // otherwise 64 < kk < nc: the general kernel writes this row
+  int32_t* out = block_idx + (size_t)h * nnz + row_ptr[i];
+  if (select) {
+    const uint32_t jj = lane < kk ? (uint32_t)key_chunk(top) : 0xFFFFFFFFu;
+    const uint32_t srt = wave_sort_u32_asc(jj, lane);
+    if (lane < kk) out[lane] = (int32_t)srt;
+    if (lane == 0) out[kk] = i;
+  } else if (kk >= nc) {                       // every earlier chunk is kept
+    for (int x = lane; x < nc; x += 64) out[x] = first + x;
+    if (lane == 0) out[nc] = i;
+  } else if (kk == 0) {
+    if (lane == 0) out[0] = i;
   }
+  // otherwise 64 < kk < nc: the general kernel writes this row
 }
 
 // General rows: more than 64 kept chunks out of a longer candidate list.
@@ -273,7 +270,7 @@ __global__ __launch_bounds__(kWideThreads) void route_wide_kernel(
 template <int D>
 hipError_t launch_route_d(const Plan& p, const float* q_sum, const float* k_sum, const int32_t* row_ptr,
                           int64_t nnz, int32_t* block_idx, bool wide_rows, hipStream_t stream) {
-  dim3 grid((p.C + kRowsPerWave - 1) / kRowsPerWave, (p.Hq + kWaves - 1) / kWaves);
+  dim3 grid(p.C, (p.Hq + kWaves - 1) / kWaves);
   hipLaunchKernelGGL(route_kernel<D>, grid, dim3(kWaves * 64), 0, stream, q_sum, k_sum, row_ptr,
                      p.seq_chunk_start, block_idx, p.B, p.C, p.Hq, p.Hkv, (long long)nnz);
   hipError_t err = hipGetLastError();
