@@ -425,7 +425,11 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
     if (wave_rows) {
       if (needs_mask(t0)) apply_mask(sc, t0);
       float alpha = 1.f;
+      // The half with the softmax issues first when both waves of the SIMD are ready: its VALU chain
+      // is the latency-critical one, and the other wave's PV MFMAs fill the gaps.
+      __builtin_amdgcn_s_setprio(2);
       region_a(std::true_type{}, std::true_type{}, k_read, sn, sc, alpha);
+      __builtin_amdgcn_s_setprio(0);
       if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {   // a running max moved
 #pragma unroll
         for (int db = 0; db < GE::DBLK; ++db)
