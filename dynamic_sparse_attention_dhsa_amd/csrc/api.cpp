@@ -160,6 +160,8 @@ dhsa_status dhsa_sparse_prefill(const dhsa_layout* layout, const void* q, const 
       out == nullptr)
     return DHSA_ERR_NULL_ARG;
   hipStream_t s = (hipStream_t)stream;
+  // the bf16 kernel addresses one KV head's rows with 32-bit buffer offsets
+  if (p.dtype == DHSA_BF16 && (int64_t)p.T * p.Hkv * p.d * 2 > (int64_t)INT32_MAX) return DHSA_ERR_UNSUPPORTED;
   if (p.dtype == DHSA_BF16)
     return launched(dhsa::launch_prefill_bf16(p, q, k, v, row_ptr, nnz, block_idx, softmax_scale, out, lse, s));
   return launched(dhsa::launch_prefill_f32(p, q, k, v, row_ptr, nnz, block_idx, softmax_scale, out, lse, s));

@@ -52,6 +52,7 @@ typedef s16x4 __attribute__((address_space(3))) lds_s16x4;
 typedef void __attribute__((address_space(3))) lds_void;
 
 constexpr int kMaxWords = DHSA_MAX_WORDS;      // bitmap words per head (32 chunks each)
+constexpr int kUnion = 4;                      // bitmap row of the union (head slots use rows 0..3)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleLog2 = 8.0f;           // move the running max only past 2^8
 constexpr int kBufWord3 = 0x00020000;          // gfx9 buffer resource: raw 32-bit data
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t k_st1[GE::TILEB];
   __shared__ __attribute__((aligned(1024))) uint8_t v_st0[GE::TILEB];
   __shared__ __attribute__((aligned(1024))) uint8_t v_st1[GE::TILEB];
-  __shared__ uint32_t bm[GE::NW + 1][kMaxWords];            // per head slot, then their union
+  __shared__ uint32_t bm[kUnion + 1][kMaxWords];            // per head slot, then their union
 
   // ---- block -> (KV head, chunk, head slot, row tile); one XCD per (KV head, chunk)
   const int G = Hq / Hkv;
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
 
   // ---- kept-chunk bitmaps of the workgroup's heads
   const int nwords = (nbits + 31) >> 5;
-  for (int x = tid; x < (GE::NW + 1) * nwords; x += NT) bm[x / nwords][x % nwords] = 0u;
+  for (int x = tid; x < (kUnion + 1) * nwords; x += NT) bm[x / nwords][x % nwords] = 0u;
   __syncthreads();
   for (int x = tid; x < hp * rlen; x += NT) {
     const int hh = x / rlen, e = x - hh * rlen;
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
     const int loc = j - first;
     if (loc >= 0 && loc < nbits) {
       atomicOr(&bm[hh][loc >> 5], 1u << (loc & 31));
-      atomicOr(&bm[GE::NW][loc >> 5], 1u << (loc & 31));
+      atomicOr(&bm[kUnion][loc >> 5], 1u << (loc & 31));
     }
   }
   __syncthreads();
@@ -190,69 +191,112 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
     }
   }
 
-  // ---- tile walk, kept in scalar registers (identical in every thread of a wave)
+  // ---- tile walk, wave-uniform, in scalar registers (every value read from memory goes through
+  // readfirstlane, so the descriptors and branches built from it stay scalar).  A tile is 64 key rows
+  // in NGRP groups of GS rows, one group per LDS-writing load.  The kept chunks before the diagonal
+  // are packed back to back: a group never crosses a chunk, but a tile does, so only the last group
+  // of a chunk carries rows past its end.  The diagonal chunk follows in tiles of its own, which the
+  // causal mask needs.  Per tile: how many rows of each group are real keys of a chunk this wave's
+  // head keeps (NB bits per group), and the first key row of each of this wave's groups.
+  constexpr int GS = GE::RPD;
+  constexpr int NGRP = BK / GS;
+  constexpr int NB = 64 / NGRP;
+  constexpr uint64_t kFull = 0x0101010101010101ull * (uint64_t)(NB == 8 ? GS : (NB == 4 ? GS * 0x11 : GS * 0x55));
   struct TileRef {
-    int jl, kt, kend;      // local chunk index (-1: walk over), key range [kt, kend) of the chunk part
-    int keep;              // whether this wave's head keeps the chunk
+    int valid;               // 0: the walk is over
+    int kt;                  // tile of the diagonal chunk: its first key row; -1 for packed tiles
+    uint64_t nval;           // real, kept rows per group (NB bits each)
+    int src[GE::DPW];        // first key row of this wave's groups
   };
-  // (every field goes through readfirstlane: the walk is wave-uniform, and scalar registers keep the
-  // buffer descriptors and branches built from it scalar)
-  auto chunk_span = [&](TileRef& t) __attribute__((always_inline)) {
-    const int j = first + t.jl;
-    t.kt = __builtin_amdgcn_readfirstlane(cu_chunks[j]);
-    t.kend = __builtin_amdgcn_readfirstlane((j == i) ? diag_end : cu_chunks[j + 1]);
-    t.keep = __builtin_amdgcn_readfirstlane((bm[hw][t.jl >> 5] >> (t.jl & 31)) & 1u);
+  auto groups_mask = [](int ng) __attribute__((always_inline)) {
+    return ng * NB >= 64 ? ~0ull : ((1ull << (ng * NB)) - 1ull);
   };
-  auto next_tile = [&](TileRef t) __attribute__((always_inline)) {
-    if (t.jl < 0) return t;
-    t.kt += BK;
-    if (t.kt >= t.kend) {
-      t.jl = __builtin_amdgcn_readfirstlane(next_set(bm[GE::NW], t.jl + 1, nbits));
-      if (t.jl >= 0) chunk_span(t);
+  auto rf = [](int x) __attribute__((always_inline)) { return __builtin_amdgcn_readfirstlane(x); };
+  // cursor: local chunk cj (-1: done), row offset coff in it, and the chunk's first row, length and
+  // keep bit for this wave's head, fetched once per chunk
+  int cj, coff = 0, cr0 = 0, clen = 0, ckeep = 0;
+  auto enter = [&](int x) __attribute__((always_inline)) {
+    cj = x;
+    coff = 0;
+    if (cj >= 0) {
+      cr0 = rf(cu_chunks[first + cj]);
+      clen = (first + cj == i) ? diag_end - cr0 : rf(cu_chunks[first + cj + 1]) - cr0;
+      ckeep = rf((bm[hw][cj >> 5] >> (cj & 31)) & 1u);
+    }
+  };
+  enter(rf(next_set(bm[kUnion], 0, nbits)));
+  auto build = [&]() __attribute__((always_inline)) {
+    TileRef t;
+    t.valid = cj >= 0;
+    t.kt = -1;
+    t.nval = 0;
+#pragma unroll
+    for (int m = 0; m < GE::DPW; ++m) t.src[m] = 0;
+    if (cj < 0) return t;
+    if (first + cj == i) {                   // diagonal chunk: contiguous rows up to diag_end
+      t.kt = cr0 + coff;
+      const int nrows = min(BK, clen - coff);
+      const int full = nrows / GS, rem = nrows % GS;
+      t.nval = (kFull & groups_mask(full)) | (full < NGRP ? (uint64_t)rem << (full * NB) : 0ull);
+#pragma unroll
+      for (int m = 0; m < GE::DPW; ++m) t.src[m] = t.kt + GS * (wave * GE::DPW + m);
+      coff += BK;
+      if (coff >= clen) cj = -1;
+      return t;
+    }
+    int slot = 0;
+    while (slot < NGRP) {                    // pack groups from consecutive kept chunks
+      const int left = clen - coff;
+      if (left > 0) {
+        const int ngr = min((left + GS - 1) / GS, NGRP - slot);
+        const int last = min(GS, left - GS * (ngr - 1));
+        if (ckeep) t.nval |= ((kFull & groups_mask(ngr - 1)) | ((uint64_t)last << ((ngr - 1) * NB))) << (slot * NB);
+#pragma unroll
+        for (int m = 0; m < GE::DPW; ++m) {
+          const int g = wave * GE::DPW + m - slot;
+          if (g >= 0 && g < ngr) t.src[m] = cr0 + coff + GS * g;
+        }
+        slot += ngr;
+        coff += GS * ngr;
+      }
+      if (coff >= clen) {                    // chunk done: on to the next kept one
+        enter(rf(next_set(bm[kUnion], cj + 1, nbits)));
+        if (cj < 0 || first + cj == i) break;   // the diagonal chunk starts a tile of its own
+      }
     }
     return t;
   };
 
   // ---- staging: LDS-writing buffer loads.  Load m of this wave writes the 1 KB at tile byte
-  // (wave * DPW + m) * 1024, lane by lane in 16-byte steps: tile row RPD * (wave * DPW + m) + lane / SLOTS,
-  // physical slot lane % SLOTS, which receives logical granule slot ^ swizzle(row).  The row block
-  // goes into the scalar offset; the swizzle splits into the lane part below and a constant of m.
-  // Every load of a tile writes all of its stage: rows past the last token are out of the buffer
-  // range and arrive as zeros.
+  // (wave * DPW + m) * 1024, lane by lane in 16-byte steps: tile row GS * (wave * DPW + m) + lane / SLOTS,
+  // physical slot lane % SLOTS, which receives logical granule slot ^ swizzle(row); the swizzle splits
+  // into the lane part below and a constant of m.  The key row of the group is added to the lane's
+  // offset (not the scalar one), so the buffer's range check covers it: rows past the last token are
+  // out of range and arrive as zeros, and nothing past the tensors is read.
   const int row_in = lane / GE::SLOTS, slot = lane % GE::SLOTS;
   const int row_bytes = Hkv * D * 2;                       // global stride of one token's KV head row
-  const int vk_lane = row_in * row_bytes + (slot ^ GE::kswz(row_in)) * 16;
-  const int vv_lane = row_in * row_bytes + (slot ^ GE::vswz(row_in)) * 16;
-  const int soff_wave = wave * GE::DPW * GE::RPD * row_bytes;
-  // buffer range: this KV head's rows from the tile start to the last token (nothing past T is read)
-  auto tile_rsrc = [&](const uint16_t* base_ptr, const TileRef& t) __attribute__((always_inline)) {
-    const int kt = __builtin_amdgcn_readfirstlane(t.kt);
-    const long long rows_left = (long long)(T - kt) * Hkv - gk;
-    const long long cap = (long long)BK * Hkv * D * 2;
-    const int nbytes = (int)min(rows_left * D * 2, cap);
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base_ptr + ((size_t)kt * Hkv + gk) * D), (short)0, nbytes,
-                                             kBufWord3);
-  };
+  const int row0 = GE::RPD * GE::DPW * wave + row_in;      // tile row of this lane in the wave's first load
+  const int vk_lane = row_in * row_bytes + (slot ^ GE::kswz(row0)) * 16;
+  const int vv_lane = row_in * row_bytes + (slot ^ GE::vswz(row0)) * 16;
+  const int kv_bytes = (int)(((long long)T * Hkv - gk) * D * 2);   // this KV head's rows, up to the last token
+  const __amdgpu_buffer_rsrc_t rsrc_k =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(k + (size_t)gk * D), (short)0, kv_bytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t rsrc_v =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(v + (size_t)gk * D), (short)0, kv_bytes, kBufWord3);
   auto load_k = [&](const TileRef& t, uint8_t* dst) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(k, t);
 #pragma unroll
     for (int m = 0; m < GE::DPW; ++m) {
-      // (the offsets are named first: clang drops the host stub of the kernel when a constexpr call
+      // (the offset is named first: clang drops the host stub of the kernel when a constexpr call
       // sits directly in this builtin's argument list)
-      const int voff = vk_lane ^ (GE::kswz(GE::RPD * m) * 16);
-      const int soff = soff_wave + m * GE::RPD * row_bytes;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + (wave * GE::DPW + m) * 1024), 16, voff, soff, 0, 0);
+      const int voff = (vk_lane ^ (GE::kswz(GE::RPD * m) * 16)) + t.src[m] * row_bytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_k, (lds_void*)(dst + (wave * GE::DPW + m) * 1024), 16, voff, 0, 0, 0);
     }
   };
   auto load_v = [&](const TileRef& t, uint8_t* dst) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(v, t);
 #pragma unroll
     for (int m = 0; m < GE::DPW; ++m) {
-      // (the offsets are named first: clang drops the host stub of the kernel when a constexpr call
-      // sits directly in this builtin's argument list)
-      const int voff = vv_lane ^ (GE::vswz(GE::RPD * m) * 16);
-      const int soff = soff_wave + m * GE::RPD * row_bytes;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + (wave * GE::DPW + m) * 1024), 16, voff, soff, 0, 0);
+      const int voff = (vv_lane ^ (GE::vswz(GE::RPD * m) * 16)) + t.src[m] * row_bytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_v, (lds_void*)(dst + (wave * GE::DPW + m) * 1024), 16, voff, 0, 0, 0);
     }
   };
 
@@ -280,23 +324,42 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
   const float grow_raw = kRescaleLog2 / c2;
   const f32x16 zero16 = {};
 
-  // S^T[b][r] holds tile key 32b + 8(r/4) + 4*half + r%4 of query `col`
-  // masking: tiles cut by the chunk end, tiles of chunks this head does not keep, and tiles of the
-  // diagonal chunk with a key past the wave's first query row
+  // S^T[b][r] holds tile row 32b + 8(r/4) + 4*half + r%4 of query `col`.
+  // A tile needs masking when a group has fewer real, kept rows than GS, or when it is a tile of the
+  // diagonal chunk with a key past the wave's first query row.
   auto needs_mask = [&](const TileRef& t) __attribute__((always_inline)) {
-    return t.kend - t.kt < BK || !t.keep || (first + t.jl == i && t.kt + BK - 1 > qr0);
+    return t.nval != kFull || (t.kt >= 0 && t.kt + BK - 1 > qr0);
   };
   auto apply_mask = [&](f32x16 (&s)[2], const TileRef& t) __attribute__((always_inline)) {
-    int lim = t.kend - t.kt - 1;
-    if (first + t.jl == i) lim = min(lim, tq - t.kt);
-    if (!t.keep) lim = -1;
-    lim -= 4 * half;
+    // rows past lim (in the lane's frame, which starts at row 4 * half) fail the causal test
+    const int lim = (t.kt >= 0 ? tq - t.kt : BK) - 4 * half;
+    const uint64_t nv = t.nval;
+    const int hs4 = 4 * half;
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[b][r] = (32 * b + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[b][r];
-        __builtin_amdgcn_sched_barrier(0);     // compare and select in turn, through one condition register
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int base = 32 * b + 8 * q4;    // lane-frame row of r = 4 q4 (plus 4 * half for the tile row)
+        if constexpr (GS == 4) {             // group 8b + 2q4 + half, row in group r % 4
+          const int n = (int)((nv >> (NB * (8 * b + 2 * q4) + NB * half)) & 0xF);
+          const int nn = min(n, lim - base + 1);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[b][4 * q4 + e] = (e < nn) ? s[b][4 * q4 + e] : -INFINITY;
+        } else if constexpr (GS == 8) {      // group 4b + q4, row in group 4 * half + r % 4
+          const int n = (int)((nv >> (NB * (4 * b + q4))) & 0xFF) - hs4;
+          const int nn = min(n, lim - base + 1);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[b][4 * q4 + e] = (e < nn) ? s[b][4 * q4 + e] : -INFINITY;
+        } else {                             // GS == 2: group 16b + 4q4 + 2half + e/2, row in group e % 2
+#pragma unroll
+          for (int p2 = 0; p2 < 2; ++p2) {
+            const int n = (int)((nv >> (NB * (16 * b + 4 * q4 + p2) + 2 * NB * half)) & 0x3);
+            const int nn = min(n, lim - base - 2 * p2 + 1);
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+              s[b][4 * q4 + 2 * p2 + e] = (e < nn) ? s[b][4 * q4 + 2 * p2 + e] : -INFINITY;
+          }
+        }
       }
   };
 
@@ -390,14 +453,11 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
   };
 
   // ---- prologue: K ring holds tiles 0 and 1, V ring tile 0
-  TileRef t0;
-  t0.jl = __builtin_amdgcn_readfirstlane(next_set(bm[GE::NW], 0, nbits));
-  t0.kt = 0; t0.kend = 0; t0.keep = 0;
-  if (t0.jl >= 0) chunk_span(t0);
-  TileRef t1 = next_tile(t0);
-  TileRef t2 = next_tile(t1);
-  if (t0.jl >= 0) { load_k(t0, k_st0); load_v(t0, v_st0); }
-  if (t1.jl >= 0) load_k(t1, k_st1);
+  TileRef t0 = build();
+  TileRef t1 = build();
+  TileRef t2 = build();
+  if (t0.valid) { load_k(t0, k_st0); load_v(t0, v_st0); }
+  if (t1.valid) load_k(t1, k_st1);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
 
@@ -419,9 +479,9 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
     uint8_t* const k_read = S ? k_st0 : k_st1;
     uint8_t* const v_fill = S ? v_st0 : v_st1;
     uint8_t* const v_read = S ? v_st1 : v_st0;
-    const TileRef t3 = next_tile(t2);
-    if (t2.jl >= 0) load_k(t2, k_fill);
-    if (t1.jl >= 0) load_v(t1, v_fill);
+    const TileRef t3 = build();
+    if (t2.valid) load_k(t2, k_fill);
+    if (t1.valid) load_v(t1, v_fill);
     if (wave_rows) {
       if (needs_mask(t0)) apply_mask(sc, t0);
       float alpha = 1.f;
@@ -442,9 +502,9 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
     __syncthreads();
     t0 = t1; t1 = t2; t2 = t3;
   };
-  while (t0.jl >= 0) {
+  while (t0.valid) {
     step(ic<0>{}, sA, sB);
-    if (t0.jl < 0) break;
+    if (!t0.valid) break;
     step(ic<1>{}, sB, sA);
   }
 

@@ -137,7 +137,8 @@ dhsa_status dhsa_route(const dhsa_layout* layout, const float* q_sum, const floa
  *              same format: ascending, inside the query chunk's sequence, j <= i,
  *              with the diagonal present)
  *   lse        device [Hq, T] float32 or NULL
- * out (and lse) are written completely. */
+ * out (and lse) are written completely.  bf16 additionally needs k and v below
+ * 2 GiB each (T * Hkv * head_dim * 2 bytes): larger returns UNSUPPORTED. */
 dhsa_status dhsa_sparse_prefill(const dhsa_layout* layout, const void* q, const void* k,
                                 const void* v, const int32_t* row_ptr, const int32_t* h_row_ptr,
                                 int64_t nnz, const int32_t* block_idx, float softmax_scale,

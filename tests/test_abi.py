@@ -137,6 +137,21 @@ def test_too_many_chunks_per_sequence_is_unsupported():
     assert lib.dhsa_validate_layout(m.ref()) == UNSUP
 
 
+def test_bf16_prefill_needs_kv_below_2gib():
+    """The bf16 kernel addresses a KV head's rows with 32-bit buffer offsets: 2^20 tokens x 8 KV heads
+    x 128 dims x 2 bytes = 2 GiB is refused before launch, although the layout itself is valid."""
+    lib = Bd.load_library()
+    T, n = 1 << 20, 128
+    C = T // n
+    cc = np.arange(0, T + 1, n, dtype=np.int32)
+    m = Mirror([0, T], cc, [0, C], Hq=8, Hkv=8, d=128)
+    rp = np.arange(C + 1, dtype=np.int32)
+    assert lib.dhsa_sparse_prefill(m.ref(), FAKE, FAKE, FAKE, FAKE, rp.ctypes.data, C, FAKE, 0.1, FAKE, None,
+                                   None) == UNSUP
+    f32 = Mirror([0, T], cc, [0, C], Hq=8, Hkv=8, d=128, dtype=0)
+    assert lib.dhsa_validate_layout(f32.ref()) == OK
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     lay = Bd.Layout.__new__(Bd.Layout)
