@@ -4,5 +4,6 @@ Only tests/, ``__graft_entry__.smoke()`` and bench.py's ``cpu_baseline`` leg
 import this package.  It shares no code with the HIP path.
 """
 from .dhsa_oracle import (attend, chunk_scores, chunk_sequence, chunk_summaries,  # noqa: F401
-                          dense_attention, kept_token_mask, prefill, route, route_plan,
-                          select_key_chunks, token_importance, validate_layout)
+                          dense_attention, group_chunk_scores, kept_token_mask, prefill, route,
+                          route_grouped, route_plan, select_key_chunks, token_importance,
+                          validate_layout)

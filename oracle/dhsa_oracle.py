@@ -116,6 +116,34 @@ def chunk_scores(q_sum, k_sum, seq_chunk_start) -> np.ndarray:
     return S
 
 
+def group_chunk_scores(q_sum, k_sum, seq_chunk_start) -> np.ndarray:
+    """Causal chunk similarity of each GQA group, ``[Hkv, C, C]`` float32.
+
+    The pages do not fix the granularity at which grouped-query heads are
+    routed.  This variant routes once per KV head: the score of query chunk i
+    and key chunk j for KV head g is the sum, over the query heads h of g's
+    group, of their similarities q_sum[i,h] . k_sum[j,g] [P2 Abstract:
+    chunk-level similarity; P3 Abstract: causal].  Summed in float64, rounded
+    once to float32; NaN outside the causal same-sequence region.
+    """
+    qs = np.asarray(q_sum, np.float64)
+    ks = np.asarray(k_sum, np.float64)
+    C, Hq, _ = qs.shape
+    Hkv = ks.shape[1]
+    G = Hq // Hkv
+    sc = np.asarray(seq_chunk_start, np.int64)
+    S = np.full((Hkv, C, C), np.nan, np.float32)
+    for b in range(sc.size - 1):
+        c0, c1 = sc[b], sc[b + 1]
+        lower = np.tri(c1 - c0, dtype=bool)         # j <= i
+        for g in range(Hkv):
+            full = np.zeros((c1 - c0, c1 - c0))
+            for h in range(g * G, (g + 1) * G):
+                full += qs[c0:c1, h, :] @ ks[c0:c1, g, :].T
+            S[g, c0:c1, c0:c1] = np.where(lower, full, np.nan).astype(np.float32)
+    return S
+
+
 # ----------------------------------------------------------------------------- step 3: keep decision
 
 def route_plan(seq_chunk_start, topk) -> Tuple[np.ndarray, int]:
@@ -160,6 +188,25 @@ def route(q_sum, k_sum, seq_chunk_start, topk):
         for i in range(C):
             kept = select_key_chunks(S[h, i], int(sc[seq[i]]), i, int(topk[i]))
             block_idx[h, row_ptr[i]:row_ptr[i + 1]] = kept
+    return row_ptr, block_idx, S
+
+
+def route_grouped(q_sum, k_sum, seq_chunk_start, topk):
+    """Routing once per KV head (see ``group_chunk_scores``): every query head of a
+    group keeps its group's chunks.  Returns ``(row_ptr [C+1], block_idx [Hq, nnz],
+    scores [Hkv, C, C])``, with the same row layout and selection rule as ``route``."""
+    S = group_chunk_scores(q_sum, k_sum, seq_chunk_start)
+    Hkv, C, _ = S.shape
+    Hq = np.asarray(q_sum).shape[1]
+    G = Hq // Hkv
+    row_ptr, nnz = route_plan(seq_chunk_start, topk)
+    sc = np.asarray(seq_chunk_start, np.int64)
+    seq = chunk_sequence(sc)
+    block_idx = np.empty((Hq, nnz), np.int32)
+    for g in range(Hkv):
+        for i in range(C):
+            kept = select_key_chunks(S[g, i], int(sc[seq[i]]), i, int(topk[i]))
+            block_idx[g * G:(g + 1) * G, row_ptr[i]:row_ptr[i + 1]] = kept
     return row_ptr, block_idx, S
 
 
@@ -261,15 +308,16 @@ def dense_attention(q, k, v, cu_seqlens, softmax_scale: float):
 # ----------------------------------------------------------------------------- whole path
 
 def prefill(q, k, v, cu_seqlens, cu_chunks, seq_chunk_start, topk, softmax_scale: float,
-            heads=None, chunks=None):
-    """Summaries, routing and sparse attention in the pages' order.
+            heads=None, chunks=None, grouped: bool = False):
+    """Summaries, routing (per query head, or per KV head when ``grouped``) and sparse
+    attention in the pages' order.
 
     Returns a dict with ``q_sum, k_sum, scores, row_ptr, block_idx, out, lse``.
     """
     validate_layout(cu_seqlens, cu_chunks, seq_chunk_start)
     q_sum = chunk_summaries(q, cu_chunks)
     k_sum = chunk_summaries(k, cu_chunks)
-    row_ptr, block_idx, S = route(q_sum, k_sum, seq_chunk_start, topk)
+    row_ptr, block_idx, S = (route_grouped if grouped else route)(q_sum, k_sum, seq_chunk_start, topk)
     out, lse = attend(q, k, v, cu_chunks, row_ptr, block_idx, softmax_scale, heads, chunks)
     return dict(q_sum=q_sum, k_sum=k_sum, scores=S, row_ptr=row_ptr, block_idx=block_idx,
                 out=out, lse=lse)

@@ -310,6 +310,63 @@ def pin_ragged_equals_separate(O):
             assert np.array_equal(a, p), (b, i)
 
 
+def pin_grouped_routing(O):
+    """Routing per KV head: with one query head per KV head it is the per-head routing; the kept set
+    of every (group, row) is the best-sum k-subset under the group-summed integer scores (exact, with
+    the lower-index tie rule); every head of a group gets the group's row; and it equals per-head
+    routing of the group-summed queries (chunks of 4 tokens: the sqrt(4) normalisation is exact)."""
+    rng = np.random.default_rng(21)
+    # (1) one query head per KV head
+    w = _small_workload(23, lens_per_seq=((3, 5, 2, 6, 4, 1, 7),), Hq=3, Hkv=3, d=6, topk=3)
+    qs, ks = O.chunk_summaries(w.q, w.cu_chunks), O.chunk_summaries(w.k, w.cu_chunks)
+    a, b = O.route(qs, ks, w.seq_chunk_start, w.topk), O.route_grouped(qs, ks, w.seq_chunk_start, w.topk)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert np.array_equal(a[2], b[2], equal_nan=True)
+    # (2) brute force over subsets, integer summaries, G = 2 or 3
+    for trial in range(6):
+        lens = [[1] * int(rng.integers(2, 9)) for _ in range(int(rng.integers(1, 3)))]
+        _, _, scs = _layout_from_lengths(lens)
+        C = int(scs[-1])
+        Hkv, G, d = 2, 2 + trial % 2, 3
+        lo, hi = (-1, 2) if trial % 2 else (-3, 4)
+        q_s = rng.integers(lo, hi, size=(C, Hkv * G, d)).astype(np.float32)
+        k_s = rng.integers(lo, hi, size=(C, Hkv, d)).astype(np.float32)
+        topk = rng.integers(0, 4, size=C).astype(np.int32)
+        row_ptr, bidx, _ = O.route_grouped(q_s, k_s, scs, topk)
+        cseq = _chunk_seq(scs)
+        for g in range(Hkv):
+            for i in range(C):
+                first = int(scs[cseq[i]])
+                cand = list(range(first, i))
+                kk = min(int(topk[i]), len(cand))
+                sc = {j: sum(int(np.dot(q_s[i, h].astype(np.int64), k_s[j, g].astype(np.int64)))
+                             for h in range(g * G, (g + 1) * G)) for j in cand}
+                best = None
+                for sub in itertools.combinations(cand, kk):
+                    key = (-sum(sc[j] for j in sub), sub)
+                    if best is None or key < best:
+                        best = key
+                want = sorted(best[1]) + [i]
+                for h in range(g * G, (g + 1) * G):
+                    got = bidx[h, row_ptr[i]:row_ptr[i + 1]].tolist()
+                    assert got == want, (trial, g, h, i, got, want)
+    # (3) the group-summed query, routed per head
+    Hkv, G, d, n = 2, 3, 4, 4
+    lens = [[n] * 7, [n] * 5]
+    cu_seqlens, cu_chunks, scs = _layout_from_lengths(lens)
+    T = int(cu_seqlens[-1])
+    q = rng.integers(-2, 3, size=(T, Hkv * G, d)).astype(np.float32)
+    k = rng.integers(-2, 3, size=(T, Hkv, d)).astype(np.float32)
+    topk = rng.integers(0, 5, size=int(scs[-1])).astype(np.int32)
+    grouped = O.route_grouped(O.chunk_summaries(q, cu_chunks), O.chunk_summaries(k, cu_chunks), scs, topk)
+    qg = q.reshape(T, Hkv, G, d).sum(axis=2)
+    single = O.route(O.chunk_summaries(qg, cu_chunks), O.chunk_summaries(k, cu_chunks), scs, topk)
+    assert np.array_equal(grouped[2], single[2], equal_nan=True)
+    for g in range(Hkv):
+        for h in range(g * G, (g + 1) * G):
+            assert np.array_equal(grouped[1][h], single[1][g]), (g, h)
+
+
 ALL_PINS = [pin_golden, pin_summary_closed_forms, pin_scores_bruteforce, pin_topk_bruteforce,
             pin_kept_invariants, pin_dense_special_case, pin_token_level_bruteforce, pin_row_sum_and_lse,
-            pin_causality, pin_gqa_and_permutation, pin_ragged_equals_separate]
+            pin_causality, pin_gqa_and_permutation, pin_ragged_equals_separate, pin_grouped_routing]

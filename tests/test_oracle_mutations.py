@@ -41,6 +41,12 @@ MUTATIONS = {
     "lse_without_max": ("LSE[h, s_i:e_i] = m[:, 0] + np.log(lsum[:, 0])", "LSE[h, s_i:e_i] = np.log(lsum[:, 0])"),
     "values_from_wrong_head": ("O[s_i:e_i, h, :] = (P @ v[keys, g, :].astype(np.float64)) / lsum",
                                "O[s_i:e_i, h, :] = (P @ v[keys, 0, :].astype(np.float64)) / lsum"),
+    "group_max_instead_of_sum": ("full += qs[c0:c1, h, :] @ ks[c0:c1, g, :].T",
+                                 "full = np.maximum(full, qs[c0:c1, h, :] @ ks[c0:c1, g, :].T)"),
+    "group_wrong_heads": ("for h in range(g * G, (g + 1) * G):\n                full +=",
+                          "for h in range(g, g + G):\n                full +="),
+    "group_row_to_first_head_only": ("block_idx[g * G:(g + 1) * G, row_ptr[i]:row_ptr[i + 1]] = kept",
+                                     "block_idx[g * G, row_ptr[i]:row_ptr[i + 1]] = kept"),
     "unnormalised_output": ("O[s_i:e_i, h, :] = (P @ v[keys, g, :].astype(np.float64)) / lsum",
                             "O[s_i:e_i, h, :] = (P @ v[keys, g, :].astype(np.float64))"),
 }
