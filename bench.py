@@ -102,7 +102,7 @@ def traffic_record(workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, topk, budget_s: float):
+def cpu_baseline(w, topk, budget_s: float, grouped: bool = False):
     """The CPU oracle (as it stands) on a bounded sample of the same workload."""
     import oracle
     try:
@@ -116,7 +116,7 @@ def cpu_baseline(w, topk, budget_s: float):
     ks = oracle.chunk_summaries(kf, w.cu_chunks)
     t_sum = time.perf_counter() - t0
     t0 = time.perf_counter()
-    rp, bi, _ = oracle.route(qs, ks, w.seq_chunk_start, topk)
+    rp, bi, _ = (oracle.route_grouped if grouped else oracle.route)(qs, ks, w.seq_chunk_start, topk)
     t_route = time.perf_counter() - t0
     rng = np.random.default_rng(0)
     rows = [(int(rng.integers(w.num_q_heads)), int(rng.integers(w.total_chunks))) for _ in range(4096)]
@@ -149,6 +149,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3, help="named workload 0..4 (3 = 128K headline)")
+    ap.add_argument("--routing", choices=("head", "kv-group"), default="head",
+                    help="route per query head (default) or once per KV head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for the baseline")
     args = ap.parse_args()
@@ -168,6 +170,7 @@ def main() -> int:
     torch.cuda.set_device(0)
     print(f"[bench] generating workload {args.config}", file=sys.stderr, flush=True)
     w = W.make_config(args.config)
+    grouped = args.routing == "kv-group"
     bf16 = w.dtype == "bf16"
     tdt = torch.bfloat16 if bf16 else torch.float32
 
@@ -191,7 +194,7 @@ def main() -> int:
         D.chunk_summarize(layout, q, k, q_sum, k_sum)
         if ev is not None:
             ev[1].record(stream)
-        D.route(layout, plan, q_sum, k_sum, block_idx)
+        D.route(layout, plan, q_sum, k_sum, block_idx, grouped=grouped)
         if ev is not None:
             ev[2].record(stream)
         D.sparse_prefill(layout, plan, q, k, v, block_idx, w.softmax_scale, out=out)
@@ -238,7 +241,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": T, "num_seqs": w.num_seqs, "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": d, "chunks": C,
-                   "topk": int(w.topk.max()) if C else 0, "parallelism": "single-gpu"},
+                   "topk": int(w.topk.max()) if C else 0, "routing": "per_kv_head" if grouped else "per_q_head",
+                   "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel" if bf16 else "prefill_f32_kernel",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": traffic_record(w.name) if bf16 else None,
@@ -258,7 +262,7 @@ def main() -> int:
     result["stages"]["stages12_frac_of_copy"] = (b1 + b2) / (t1 + t2) / 1e9 / peaks["copy_1GiB_GBps"]
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w, w.topk, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(w, w.topk, args.cpu_budget, grouped)
     print(json.dumps(result), flush=True)
     return 0
 

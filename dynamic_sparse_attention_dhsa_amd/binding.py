@@ -26,7 +26,7 @@ STATUS_NAMES = {0: "DHSA_OK", 1: "DHSA_ERR_NULL_ARG", 2: "DHSA_ERR_BAD_SHAPE", 3
 
 # every entry point declared in include/dhsa.h
 EXPORTS = ("dhsa_abi_version", "dhsa_status_str", "dhsa_validate_layout", "dhsa_route_plan",
-           "dhsa_chunk_summarize", "dhsa_route", "dhsa_sparse_prefill")
+           "dhsa_chunk_summarize", "dhsa_route", "dhsa_route_grouped", "dhsa_sparse_prefill")
 
 
 class DhsaError(RuntimeError):
@@ -67,8 +67,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dhsa_route_plan.argtypes = [lp, vp, vp, ctypes.POINTER(i64)]
     lib.dhsa_chunk_summarize.restype = i32
     lib.dhsa_chunk_summarize.argtypes = [lp, vp, vp, vp, vp, vp]
-    lib.dhsa_route.restype = i32
-    lib.dhsa_route.argtypes = [lp, vp, vp, vp, vp, i64, vp, vp]
+    for name in ("dhsa_route", "dhsa_route_grouped"):
+        getattr(lib, name).restype = i32
+        getattr(lib, name).argtypes = [lp, vp, vp, vp, vp, i64, vp, vp]
     lib.dhsa_sparse_prefill.restype = i32
     lib.dhsa_sparse_prefill.argtypes = [lp, vp, vp, vp, vp, vp, i64, vp, ctypes.c_float, vp, vp, vp]
     if lib.dhsa_abi_version() != 1:
@@ -179,16 +180,19 @@ def chunk_summarize(layout: Layout, q: torch.Tensor, k: torch.Tensor,
 
 
 def route(layout: Layout, plan: RoutePlan, q_sum: torch.Tensor, k_sum: torch.Tensor,
-          block_idx: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Stage 2 (dhsa_route): kept key chunks, int32 [Hq, nnz], rows ascending with the diagonal last."""
+          block_idx: Optional[torch.Tensor] = None, grouped: bool = False) -> torch.Tensor:
+    """Stage 2 (dhsa_route, or dhsa_route_grouped when ``grouped``: one selection per KV head, shared
+    by its query heads): kept key chunks, int32 [Hq, nnz], rows ascending with the diagonal last."""
     if block_idx is None:
         block_idx = torch.empty((layout.num_q_heads, plan.nnz), dtype=torch.int32, device=q_sum.device)
     for t, name in ((q_sum, "q_sum"), (k_sum, "k_sum")):
         if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
             raise DhsaError(2, name, "expected a contiguous float32 GPU tensor")
-    _check(load_library().dhsa_route(ctypes.byref(layout.struct), _ptr(q_sum), _ptr(k_sum), _ptr(plan.d_row_ptr),
-                                     plan.h_row_ptr.ctypes.data, plan.nnz, _ptr(block_idx), _stream()),
-           "dhsa_route")
+    name = "dhsa_route_grouped" if grouped else "dhsa_route"
+    _check(getattr(load_library(), name)(ctypes.byref(layout.struct), _ptr(q_sum), _ptr(k_sum),
+                                         _ptr(plan.d_row_ptr), plan.h_row_ptr.ctypes.data, plan.nnz,
+                                         _ptr(block_idx), _stream()),
+           name)
     return block_idx
 
 
@@ -216,13 +220,14 @@ def sparse_prefill(layout: Layout, plan: RoutePlan, q: torch.Tensor, k: torch.Te
 
 
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens, cu_chunks, seq_chunk_start, topk,
-            softmax_scale: Optional[float] = None, return_lse: bool = False):
-    """The whole path: summaries, routing, sparse attention.  Returns a dict of device tensors."""
+            softmax_scale: Optional[float] = None, return_lse: bool = False, grouped: bool = False):
+    """The whole path: summaries, routing (per query head, or per KV head when ``grouped``), sparse
+    attention.  Returns a dict of device tensors."""
     layout = Layout(cu_seqlens, cu_chunks, seq_chunk_start, q.shape[1], k.shape[1], q.shape[2], q.dtype,
                     device=q.device)
     plan = RoutePlan(layout, topk)
     q_sum, k_sum = chunk_summarize(layout, q, k)
-    block_idx = route(layout, plan, q_sum, k_sum)
+    block_idx = route(layout, plan, q_sum, k_sum, grouped=grouped)
     res = sparse_prefill(layout, plan, q, k, v, block_idx, softmax_scale, return_lse=return_lse)
     out, lse = res if return_lse else (res, None)
     return dict(out=out, lse=lse, q_sum=q_sum, k_sum=k_sum, row_ptr=plan.h_row_ptr, block_idx=block_idx,

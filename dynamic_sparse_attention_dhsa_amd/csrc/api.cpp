@@ -129,9 +129,9 @@ dhsa_status dhsa_chunk_summarize(const dhsa_layout* layout, const void* q, const
   return launched(dhsa::launch_summarize(p, q, k, q_sum, k_sum, (hipStream_t)stream));
 }
 
-dhsa_status dhsa_route(const dhsa_layout* layout, const float* q_sum, const float* k_sum,
-                       const int32_t* row_ptr, const int32_t* h_row_ptr, int64_t nnz, int32_t* block_idx,
-                       void* stream) {
+static dhsa_status route_common(const dhsa_layout* layout, const float* q_sum, const float* k_sum,
+                                const int32_t* row_ptr, const int32_t* h_row_ptr, int64_t nnz,
+                                int32_t* block_idx, bool grouped, void* stream) {
   Plan p;
   dhsa_status st = check_layout(layout, &p);
   if (st != DHSA_OK) return st;
@@ -141,7 +141,20 @@ dhsa_status dhsa_route(const dhsa_layout* layout, const float* q_sum, const floa
   if (p.C == 0) return DHSA_OK;
   if (q_sum == nullptr || k_sum == nullptr || row_ptr == nullptr || block_idx == nullptr)
     return DHSA_ERR_NULL_ARG;
-  return launched(dhsa::launch_route(p, q_sum, k_sum, row_ptr, nnz, block_idx, wide, (hipStream_t)stream));
+  return launched(dhsa::launch_route(p, q_sum, k_sum, row_ptr, nnz, block_idx, wide, grouped,
+                                     (hipStream_t)stream));
+}
+
+dhsa_status dhsa_route(const dhsa_layout* layout, const float* q_sum, const float* k_sum,
+                       const int32_t* row_ptr, const int32_t* h_row_ptr, int64_t nnz, int32_t* block_idx,
+                       void* stream) {
+  return route_common(layout, q_sum, k_sum, row_ptr, h_row_ptr, nnz, block_idx, false, stream);
+}
+
+dhsa_status dhsa_route_grouped(const dhsa_layout* layout, const float* q_sum, const float* k_sum,
+                               const int32_t* row_ptr, const int32_t* h_row_ptr, int64_t nnz,
+                               int32_t* block_idx, void* stream) {
+  return route_common(layout, q_sum, k_sum, row_ptr, h_row_ptr, nnz, block_idx, true, stream);
 }
 
 dhsa_status dhsa_sparse_prefill(const dhsa_layout* layout, const void* q, const void* k, const void* v,

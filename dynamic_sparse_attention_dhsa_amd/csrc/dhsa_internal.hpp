@@ -27,7 +27,7 @@ hipError_t launch_summarize(const Plan& p, const void* q, const void* k, float* 
 // Stage 2: kept key-chunk lists.  `wide_rows` tells whether some row keeps more than 64 earlier
 // chunks while not keeping all of them (those rows take the general sorting kernel).
 hipError_t launch_route(const Plan& p, const float* q_sum, const float* k_sum, const int32_t* row_ptr,
-                        int64_t nnz, int32_t* block_idx, bool wide_rows, hipStream_t stream);
+                        int64_t nnz, int32_t* block_idx, bool wide_rows, bool grouped, hipStream_t stream);
 
 // Stage 3: block-sparse causal prefill.
 hipError_t launch_prefill_bf16(const Plan& p, const void* q, const void* k, const void* v,

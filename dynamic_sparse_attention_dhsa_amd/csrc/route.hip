@@ -10,6 +10,10 @@
 //   ranked by (s_j descending, j ascending), plus the diagonal chunk i,
 // written ascending into its slice of the CSR block list.
 //
+// Routing once per KV head (a reading of the open GQA granularity) scores with
+// the sum of the group's query summaries instead of one head's and gives every
+// head of the group the same row.
+//
 // Ranking uses a 64-bit key (order-preserving bits of the fp32 score, then
 // the complemented chunk id), so a larger key is a better candidate and every
 // key is distinct: ties resolve to the lower chunk id exactly.
@@ -103,7 +107,7 @@ __device__ inline uint64_t merge_batch(uint64_t top, uint64_t batch, int lane) {
   return m;
 }
 
-template <int D>
+template <int D, bool GROUPED>
 __global__ __launch_bounds__(kWaves * 64) void route_kernel(
     const float* __restrict__ q_sum, const float* __restrict__ k_sum,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ seq_chunk_start,
@@ -125,7 +129,14 @@ __global__ __launch_bounds__(kWaves * 64) void route_kernel(
   const int nc = i - first;
   const int kk = row_ptr[i + 1] - row_ptr[i] - 1;
   const bool select = kk > 0 && kk < nc && kk <= kMaxTop;   // same for every head of the chunk
-  for (int x = lane; x < D; x += 64) qs[wave][x] = q_sum[((size_t)i * Hq + h) * D + x];
+  // the query side of the score: this head's summary, or (routing per KV head) the sum of the
+  // group's summaries in ascending head order
+  for (int x = lane; x < D; x += 64) {
+    float acc = q_sum[((size_t)i * Hq + (GROUPED ? g * G : h)) * D + x];
+    if constexpr (GROUPED)
+      for (int hh = 1; hh < G; ++hh) acc += q_sum[((size_t)i * Hq + g * G + hh) * D + x];
+    qs[wave][x] = acc;
+  }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -189,7 +200,7 @@ __global__ __launch_bounds__(kWaves * 64) void route_kernel(
 }
 
 // General rows: more than 64 kept chunks out of a longer candidate list.
-template <int D>
+template <int D, bool GROUPED>
 __global__ __launch_bounds__(kWideThreads) void route_wide_kernel(
     const float* __restrict__ q_sum, const float* __restrict__ k_sum,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ seq_chunk_start,
@@ -209,7 +220,13 @@ __global__ __launch_bounds__(kWideThreads) void route_wide_kernel(
   int npad = 1;
   while (npad < n) npad <<= 1;
 
-  for (int x = tid; x < D; x += kWideThreads) qrow[x] = q_sum[((size_t)i * Hq + h) * D + x];
+  for (int x = tid; x < D; x += kWideThreads) {
+    const int G = Hq / Hkv, g0 = (h / G) * G;
+    float acc = q_sum[((size_t)i * Hq + (GROUPED ? g0 : h)) * D + x];
+    if constexpr (GROUPED)
+      for (int hh = 1; hh < G; ++hh) acc += q_sum[((size_t)i * Hq + g0 + hh) * D + x];
+    qrow[x] = acc;
+  }
   for (int x = tid; x < kMaxCand / 32; x += kWideThreads) flags[x] = 0u;
   __syncthreads();
   for (int x = tid; x < npad; x += kWideThreads) {
@@ -267,29 +284,36 @@ __global__ __launch_bounds__(kWideThreads) void route_wide_kernel(
   if (tid == 0) out[kk] = i;
 }
 
-template <int D>
+template <int D, bool GROUPED>
 hipError_t launch_route_d(const Plan& p, const float* q_sum, const float* k_sum, const int32_t* row_ptr,
                           int64_t nnz, int32_t* block_idx, bool wide_rows, hipStream_t stream) {
   dim3 grid(p.C, (p.Hq + kWaves - 1) / kWaves);
-  hipLaunchKernelGGL(route_kernel<D>, grid, dim3(kWaves * 64), 0, stream, q_sum, k_sum, row_ptr,
+  hipLaunchKernelGGL((route_kernel<D, GROUPED>), grid, dim3(kWaves * 64), 0, stream, q_sum, k_sum, row_ptr,
                      p.seq_chunk_start, block_idx, p.B, p.C, p.Hq, p.Hkv, (long long)nnz);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !wide_rows) return err;
-  hipLaunchKernelGGL(route_wide_kernel<D>, dim3(p.C, p.Hq), dim3(kWideThreads), 0, stream, q_sum, k_sum,
-                     row_ptr, p.seq_chunk_start, block_idx, p.B, p.C, p.Hq, p.Hkv, (long long)nnz);
+  hipLaunchKernelGGL((route_wide_kernel<D, GROUPED>), dim3(p.C, p.Hq), dim3(kWideThreads), 0, stream, q_sum,
+                     k_sum, row_ptr, p.seq_chunk_start, block_idx, p.B, p.C, p.Hq, p.Hkv, (long long)nnz);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_route_g(const Plan& p, const float* q_sum, const float* k_sum, const int32_t* row_ptr,
+                          int64_t nnz, int32_t* block_idx, bool wide_rows, bool grouped, hipStream_t stream) {
+  return grouped ? launch_route_d<D, true>(p, q_sum, k_sum, row_ptr, nnz, block_idx, wide_rows, stream)
+                 : launch_route_d<D, false>(p, q_sum, k_sum, row_ptr, nnz, block_idx, wide_rows, stream);
 }
 
 }  // namespace
 
 hipError_t launch_route(const Plan& p, const float* q_sum, const float* k_sum, const int32_t* row_ptr,
-                        int64_t nnz, int32_t* block_idx, bool wide_rows, hipStream_t stream) {
+                        int64_t nnz, int32_t* block_idx, bool wide_rows, bool grouped, hipStream_t stream) {
   if (p.C == 0) return hipSuccess;
   switch (p.d) {
-    case 32: return launch_route_d<32>(p, q_sum, k_sum, row_ptr, nnz, block_idx, wide_rows, stream);
-    case 64: return launch_route_d<64>(p, q_sum, k_sum, row_ptr, nnz, block_idx, wide_rows, stream);
-    case 128: return launch_route_d<128>(p, q_sum, k_sum, row_ptr, nnz, block_idx, wide_rows, stream);
-    case 256: return launch_route_d<256>(p, q_sum, k_sum, row_ptr, nnz, block_idx, wide_rows, stream);
+    case 32: return launch_route_g<32>(p, q_sum, k_sum, row_ptr, nnz, block_idx, wide_rows, grouped, stream);
+    case 64: return launch_route_g<64>(p, q_sum, k_sum, row_ptr, nnz, block_idx, wide_rows, grouped, stream);
+    case 128: return launch_route_g<128>(p, q_sum, k_sum, row_ptr, nnz, block_idx, wide_rows, grouped, stream);
+    case 256: return launch_route_g<256>(p, q_sum, k_sum, row_ptr, nnz, block_idx, wide_rows, grouped, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -126,6 +126,18 @@ dhsa_status dhsa_route(const dhsa_layout* layout, const float* q_sum, const floa
                        const int32_t* row_ptr, const int32_t* h_row_ptr, int64_t nnz,
                        int32_t* block_idx, void* stream);
 
+/* Stage 2, routed once per KV head (same pages; the granularity at which
+ * grouped-query heads are routed is left open there).  For KV head g and query
+ * chunk i, every earlier chunk j of the same sequence is scored
+ *   s_j = (sum over the query heads h of g's group of q_sum[i, h, :]) . k_sum[j, g, :]
+ * (fp32; the group sum in ascending head order), selected like dhsa_route, and
+ * the group's row is written to the rows of all of its query heads, so
+ * block_idx has the same layout and dhsa_sparse_prefill takes it unchanged.
+ * Arguments, validation and errors as dhsa_route. */
+dhsa_status dhsa_route_grouped(const dhsa_layout* layout, const float* q_sum, const float* k_sum,
+                               const int32_t* row_ptr, const int32_t* h_row_ptr, int64_t nnz,
+                               int32_t* block_idx, void* stream);
+
 /* Stage 3: block-sparse causal prefill (ICML 2026 page, Abstract: tiled
  * backend; exact softmax over the kept token interactions).  Query token t of
  * chunk i, head h attends to every key u <= t lying in a kept chunk of row

@@ -38,8 +38,9 @@ def _dev(a: np.ndarray, dtype: str) -> torch.Tensor:
 class Case:
     """A workload with its device tensors, the GPU path's results and the oracle's."""
 
-    def __init__(self, w: W.Workload, topk=None):
+    def __init__(self, w: W.Workload, topk=None, grouped: bool = False):
         self.w = w
+        self.grouped = grouped
         self.topk = w.topk if topk is None else np.asarray(topk, np.int32)
         print(f"[case] {w.name} seed={w.seed} T={w.total_tokens} C={w.total_chunks} Hq={w.num_q_heads} "
               f"Hkv={w.num_kv_heads} d={w.head_dim} {w.dtype}", flush=True)
@@ -52,7 +53,12 @@ class Case:
         # oracle: summaries and routing for every row
         self.o_qs = oracle.chunk_summaries(self.qf, w.cu_chunks)
         self.o_ks = oracle.chunk_summaries(self.kf, w.cu_chunks)
-        self.o_rp, self.o_bidx, self.o_scores = oracle.route(self.o_qs, self.o_ks, w.seq_chunk_start, self.topk)
+        if grouped:     # one selection per KV head; its scores stand for every head of the group
+            self.o_rp, self.o_bidx, s_g = oracle.route_grouped(self.o_qs, self.o_ks, w.seq_chunk_start, self.topk)
+            self.o_scores = np.repeat(s_g, w.num_q_heads // w.num_kv_heads, axis=0)
+        else:
+            self.o_rp, self.o_bidx, self.o_scores = oracle.route(self.o_qs, self.o_ks, w.seq_chunk_start,
+                                                                 self.topk)
         assert np.array_equal(self.o_rp, self.plan.h_row_ptr)
 
     # GPU stages ---------------------------------------------------------------------------
@@ -66,7 +72,7 @@ class Case:
             q_sum, k_sum = D.chunk_summarize(self.layout, self.q, self.k)
         else:
             q_sum, k_sum = torch.from_numpy(q_sum).cuda(), torch.from_numpy(k_sum).cuda()
-        b = D.route(self.layout, self.plan, q_sum, k_sum)
+        b = D.route(self.layout, self.plan, q_sum, k_sum, grouped=self.grouped)
         torch.cuda.synchronize()
         return b.cpu().numpy()
 
@@ -79,7 +85,7 @@ class Case:
 
     def gpu_prefill(self):
         r = D.prefill(self.q, self.k, self.v, self.w.cu_seqlens, self.w.cu_chunks, self.w.seq_chunk_start,
-                      self.topk, self.w.softmax_scale, return_lse=True)
+                      self.topk, self.w.softmax_scale, return_lse=True, grouped=self.grouped)
         torch.cuda.synchronize()
         return r["block_idx"].cpu().numpy(), r["out"].float().cpu().numpy(), r["lse"].cpu().numpy()
 
@@ -191,6 +197,23 @@ def test_small_end_to_end(small_case):
     check_end_to_end(small_case)
 
 
+# routing once per KV head: the group's row, checked against the oracle's grouped routing, and the
+# whole path end to end with it
+GROUPED = ("bf16_d128_g4_ragged", "bf16_d128_g8_long_chunks", "bf16_d256_g2", "bf16_d64_g1", "bf16_divergent_heads",
+           "f32_d128_g2")
+
+
+@pytest.mark.parametrize("name", GROUPED)
+def test_small_grouped_routing_and_end_to_end(name):
+    case = Case(SMALL[name](), grouped=True)
+    g_b, eq, tol = check_routing(case)
+    G = case.w.num_q_heads // case.w.num_kv_heads
+    for h in range(case.w.num_q_heads):      # every head of a group carries the group's row
+        assert np.array_equal(g_b[h], g_b[(h // G) * G]), h
+    check_routing(case, case.o_qs, case.o_ks)
+    check_end_to_end(case)
+
+
 def test_budget_extremes():
     w = small([SeqSpec(800, ("uniform", 20, 80), 0, 2), SeqSpec(500, ("uniform", 10, 60), 0, 0)], 4, 2, 128, "bf16",
               21, "extremes")
@@ -291,4 +314,15 @@ def test_full_config_sampled(cfg):
     heads, chunks = _sample_rows(case)
     err, lerr = check_attention(case, heads, chunks)
     print(f"[cfg{cfg}] sampled {len(heads)}x{len(chunks)} rows: out err {err:.3e}, lse err {lerr:.3e}", flush=True)
+    check_end_to_end(case, heads, chunks)
+
+
+@pytest.mark.slow
+def test_full_config_grouped_sampled():
+    """The 128K workload routed once per KV head: every row's kept set against the oracle's grouped
+    routing, and the whole path on sampled rows."""
+    case = Case(W.make_config(3), grouped=True)
+    _, eq, tol = check_routing(case)
+    print(f"[cfg3 grouped] kept sets: {eq} equal rows, {tol} tolerated swaps", flush=True)
+    heads, chunks = _sample_rows(case)
     check_end_to_end(case, heads, chunks)
