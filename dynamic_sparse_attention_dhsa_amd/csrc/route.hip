@@ -141,21 +141,35 @@ __global__ __launch_bounds__(kWaves * 64) void route_kernel(
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
+  // shared batches: each thread holds its share of the next batch in registers while the current
+  // one is scored and merged
+  constexpr int PER = 64 * (D / 4) / (kWaves * 64);
+  float4 pre[PER];
+  auto fetch = [&](int jb) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int x = threadIdx.x + p * kWaves * 64;
+      const int row = x / (D / 4), c4 = x % (D / 4);
+      const int jj = jb + row;
+      pre[p] = jj < i ? reinterpret_cast<const float4*>(k_sum + ((size_t)jj * Hkv + g) * D)[c4]
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
   uint64_t top = 0;
   if (select) {
+    if (shared_kv) fetch(first);
     for (int jb = first; jb < i; jb += 64) {
       const int j = jb + lane;
       float acc = 0.f;
       if (shared_kv) {
         __syncthreads();                       // the previous batch has been read
-        for (int x = threadIdx.x; x < 64 * (D / 4); x += kWaves * 64) {
-          const int row = x / (D / 4), c4 = x % (D / 4);
-          const int jj = jb + row;
-          const float4 kv = jj < i ? reinterpret_cast<const float4*>(k_sum + ((size_t)jj * Hkv + g) * D)[c4]
-                                   : make_float4(0.f, 0.f, 0.f, 0.f);
-          *reinterpret_cast<float4*>(&ks[row][4 * c4]) = kv;
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+          const int x = threadIdx.x + p * kWaves * 64;
+          *reinterpret_cast<float4*>(&ks[x / (D / 4)][4 * (x % (D / 4))]) = pre[p];
         }
         __syncthreads();
+        if (jb + 64 < i) fetch(jb + 64);
 #pragma unroll 8
         for (int x = 0; x < D / 4; ++x) {
           const float4 kv = *reinterpret_cast<const float4*>(&ks[lane][4 * x]);
