@@ -56,7 +56,7 @@ dhsa_status check_layout(const dhsa_layout* L, Plan* plan) {
 }
 
 // Row pointers must be the plan of some budget: row i holds between 1 and i_loc + 1 entries.
-// Sets *wide when a row keeps more than 64 earlier chunks without keeping all of them.
+// Sets *wide when a row with more than kRouteRegCand earlier chunks keeps some but not all of them.
 dhsa_status check_row_ptr(const dhsa_layout* L, const int32_t* h_row_ptr, int64_t nnz, bool* wide) {
   if (h_row_ptr == nullptr) return DHSA_ERR_NULL_ARG;
   const int32_t* sc = L->h_seq_chunk_start;
@@ -67,7 +67,7 @@ dhsa_status check_row_ptr(const dhsa_layout* L, const int32_t* h_row_ptr, int64_
       const int64_t len = (int64_t)h_row_ptr[c + 1] - h_row_ptr[c];
       const int32_t i_loc = c - sc[b];
       if (len < 1 || len > (int64_t)i_loc + 1) return DHSA_ERR_BAD_SHAPE;
-      if (len - 1 > 64 && len - 1 < i_loc) *wide = true;
+      if (len - 1 > 0 && len - 1 < i_loc && i_loc > dhsa::kRouteRegCand) *wide = true;
     }
   }
   if ((int64_t)h_row_ptr[L->total_chunks] != nnz) return DHSA_ERR_BAD_SHAPE;

@@ -24,8 +24,10 @@ struct Plan {
 hipError_t launch_summarize(const Plan& p, const void* q, const void* k, float* q_sum, float* k_sum,
                             hipStream_t stream);
 
-// Stage 2: kept key-chunk lists.  `wide_rows` tells whether some row keeps more than 64 earlier
-// chunks while not keeping all of them (those rows take the general sorting kernel).
+// Stage 2: kept key-chunk lists.  The main routing kernel holds up to kRouteRegCand candidates
+// of a row in registers; `wide_rows` tells whether some row with more candidates than that keeps
+// some but not all of them (those rows take the general sorting kernel).
+constexpr int kRouteRegCand = 1024;
 hipError_t launch_route(const Plan& p, const float* q_sum, const float* k_sum, const int32_t* row_ptr,
                         int64_t nnz, int32_t* block_idx, bool wide_rows, bool grouped, hipStream_t stream);
 

@@ -14,28 +14,34 @@
 // the sum of the group's query summaries instead of one head's and gives every
 // head of the group the same row.
 //
-// Ranking uses a 64-bit key (order-preserving bits of the fp32 score, then
-// the complemented chunk id), so a larger key is a better candidate and every
-// key is distinct: ties resolve to the lower chunk id exactly.
+// Scores are ranked by their order-preserving bits (the fp32 order, with -0
+// equal to +0); the general kernel appends the complemented chunk id, so a
+// larger 64-bit key is a better candidate and ties resolve to the lower chunk
+// id exactly.
 //
-// Main kernel: a wave owns one q head and one query chunk (a workgroup: four q
-// heads of one chunk; chunks with the most candidates are launched first).  It
-// walks the candidates in batches of 64 (one per lane), computes the row's fp32
-// dot products (when the four heads share a KV head, each batch of K summaries
-// is staged once in LDS for all of them), and keeps the row's best 64 keys as a sorted
-// wave-wide list: a batch is bitonic-sorted across lanes, merged with the list
-// by an element-wise max against the reversed order, and re-sorted with a
-// bitonic half-cleaner cascade.  Batches that cannot beat the row's current
-// k-th key are skipped.  Rows keeping more than 64 chunks out of a longer
-// candidate list go to a general kernel that bitonic-sorts all of the row's
-// keys in LDS.
+// Main kernel: a workgroup owns one query chunk and four q heads (chunks with
+// the most candidates are launched first).  Scoring: when the four heads share
+// a KV head, each wave takes blocks of 16 candidates, four lanes per candidate
+// (each a quarter of the row), and computes all four heads' dot products (one,
+// when routing per KV head) from one read of the K summary, reduced across the
+// four lanes; otherwise each wave scores its own head, one candidate per lane.
+// The scores go to LDS.
+// Selection, one wave per head: the row's scores are loaded into registers (64
+// candidates per register), the k-th best score is found by a most-significant-
+// bit-first binary search over the order-preserving score bits (each step
+// counts the candidates at or above a trial value with wave ballots), and one
+// pass in chunk order writes those above it plus the first ones equal to it,
+// which is the (score desc, chunk asc) top-k already in ascending chunk order.
+// Rows with more candidates than the registers hold go to a general kernel
+// that bitonic-sorts all of the row's keys in LDS.
 #include "dhsa_internal.hpp"
 
 namespace dhsa {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kMaxTop = 64;
+constexpr int kRegCand = kRouteRegCand;          // candidates held in registers
+constexpr int kRegBatches = kRegCand / 64;       // 64 per batch, one per lane
 constexpr int kWideThreads = 256;
 constexpr int kMaxCand = 8192;
 
@@ -50,61 +56,50 @@ __device__ inline uint64_t rank_key(float s, int j) {
 
 __device__ inline int key_chunk(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
 
-__device__ inline uint64_t shfl_xor_u64(uint64_t x, int m) {
-  uint32_t lo = __shfl_xor((unsigned)x, m);
-  uint32_t hi = __shfl_xor((unsigned)(x >> 32), m);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ inline uint64_t shfl_u64(uint64_t x, int src) {
-  uint32_t lo = __shfl((unsigned)x, src);
-  uint32_t hi = __shfl((unsigned)(x >> 32), src);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// Bitonic sort of one key per lane across the wave; ascending (lane 0 smallest)
-// when `ascending`, else descending.
-__device__ inline uint64_t wave_sort(uint64_t key, int lane, bool ascending) {
+// Selection over the scores held in registers (ob[b]: ordered bits of candidate first + 64 b +
+// lane, 0 where there is no candidate; a finite score never maps to 0 and every trial value is at
+// least 1, so empty slots never count).  NB is the number of batches in use, fixed at compile time
+// so the per-bit count is straight-line code.  Writes the row's kk kept chunks, ascending.
+template <int NB>
+__device__ inline void select_and_write(const uint32_t (&ob)[kRegBatches], int kk, int first, int lane,
+                                        int32_t* __restrict__ out) {
+  // thr: the largest value with at least kk candidates at or above it, i.e. the kk-th best score
+  uint32_t thr = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t t = thr | (1u << bit);
+    int cnt = 0;
 #pragma unroll
-  for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      uint64_t other = shfl_xor_u64(key, stride);
-      bool lower = (lane & stride) == 0;
-      bool block_up = ((lane & size) == 0) == ascending;   // direction of this block
-      bool keep_small = (lower == block_up);
-      key = keep_small ? (key < other ? key : other) : (key > other ? key : other);
-    }
+    for (int b = 0; b < NB; ++b) cnt += __popcll(__ballot(ob[b] >= t));
+    if (cnt >= kk) thr = t;
   }
-  return key;
+  // Write in chunk order those above thr, then the first ones equal to it until kk are written.
+  int above = 0;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) above += __popcll(__ballot(ob[b] > thr));
+  const int need = kk - above;
+  const uint64_t below = (1ull << lane) - 1ull;
+  int pos = 0, eq_seen = 0;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const bool eq = ob[b] == thr;              // thr >= 1, so only real candidates
+    const uint64_t eqm = __ballot(eq);
+    const bool keep = ob[b] > thr || (eq && eq_seen + __popcll(eqm & below) < need);
+    eq_seen += __popcll(eqm);
+    const uint64_t km = __ballot(keep);
+    if (keep) out[pos + __popcll(km & below)] = first + 64 * b + lane;
+    pos += __popcll(km);
+  }
 }
 
-__device__ inline uint32_t wave_sort_u32_asc(uint32_t v, int lane) {
-#pragma unroll
-  for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      uint32_t other = __shfl_xor(v, stride);
-      bool lower = (lane & stride) == 0;
-      bool block_up = (lane & size) == 0;
-      bool keep_small = (lower == block_up);
-      v = keep_small ? min(v, other) : max(v, other);
-    }
+template <int NB>
+__device__ inline void select_dispatch(int nb, const uint32_t (&ob)[kRegBatches], int kk, int first, int lane,
+                                       int32_t* __restrict__ out) {
+  if constexpr (NB > kRegBatches) {
+    return;
+  } else {
+    if (nb == NB) select_and_write<NB>(ob, kk, first, lane, out);
+    else select_dispatch<NB + 1>(nb, ob, kk, first, lane, out);
   }
-  return v;
-}
-
-// `top` is sorted descending across lanes; returns the best 64 of top U batch, sorted descending.
-__device__ inline uint64_t merge_batch(uint64_t top, uint64_t batch, int lane) {
-  uint64_t b = wave_sort(batch, lane, /*ascending=*/true);
-  uint64_t m = top > b ? top : b;                 // bitonic: falls, then rises
-#pragma unroll
-  for (int stride = 32; stride > 0; stride >>= 1) {
-    uint64_t other = shfl_xor_u64(m, stride);
-    bool lower = (lane & stride) == 0;
-    m = lower ? (m > other ? m : other) : (m < other ? m : other);
-  }
-  return m;
 }
 
 template <int D, bool GROUPED>
@@ -112,15 +107,17 @@ __global__ __launch_bounds__(kWaves * 64) void route_kernel(
     const float* __restrict__ q_sum, const float* __restrict__ k_sum,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ seq_chunk_start,
     int32_t* __restrict__ block_idx, int B, int C, int Hq, int Hkv, long long nnz) {
-  __shared__ float qs[kWaves][D];
-  __shared__ __attribute__((aligned(16))) float ks[64][D + 4];   // a batch of K summaries (padded rows)
+  __shared__ __attribute__((aligned(16))) float qs[kWaves][D];
+  __shared__ float sc[kWaves][kRegCand];       // the four rows' scores
+  const int nhb = (Hq + kWaves - 1) / kWaves;  // head blocks per chunk
+  const int i = C - 1 - (int)blockIdx.x / nhb; // latest chunks (most candidates) first, all heads
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int h = blockIdx.y * kWaves + wave;
-  const int i = C - 1 - blockIdx.x;            // latest chunks (most candidates) first
+  const int h0 = ((int)blockIdx.x % nhb) * kWaves;
+  const int h = h0 + wave;
   const int G = Hq / Hkv;
-  // When the workgroup's four q heads share one KV head, each batch of K summaries is loaded once
-  // into LDS for all of them (block-uniform; then Hq % 4 == 0 and no wave leaves early).
+  // When the workgroup's four q heads share one KV head, candidates are scored for all four at
+  // once (block-uniform; then Hq % 4 == 0 and no wave leaves early).
   const bool shared_kv = G % kWaves == 0;
   if (h >= Hq) return;                         // only when Hq % 4 != 0: no block barrier is used then
   const int g = h / G;
@@ -128,92 +125,101 @@ __global__ __launch_bounds__(kWaves * 64) void route_kernel(
   const int first = seq_chunk_start[seq_of_chunk(seq_chunk_start, B, i)];
   const int nc = i - first;
   const int kk = row_ptr[i + 1] - row_ptr[i] - 1;
-  const bool select = kk > 0 && kk < nc && kk <= kMaxTop;   // same for every head of the chunk
-  // the query side of the score: this head's summary, or (routing per KV head) the sum of the
-  // group's summaries in ascending head order
-  for (int x = lane; x < D; x += 64) {
-    float acc = q_sum[((size_t)i * Hq + (GROUPED ? g * G : h)) * D + x];
-    if constexpr (GROUPED)
-      for (int hh = 1; hh < G; ++hh) acc += q_sum[((size_t)i * Hq + g * G + hh) * D + x];
-    qs[wave][x] = acc;
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-  // shared batches: each thread holds its share of the next batch in registers while the current
-  // one is scored and merged
-  constexpr int PER = 64 * (D / 4) / (kWaves * 64);
-  float4 pre[PER];
-  auto fetch = [&](int jb) {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int x = threadIdx.x + p * kWaves * 64;
-      const int row = x / (D / 4), c4 = x % (D / 4);
-      const int jj = jb + row;
-      pre[p] = jj < i ? reinterpret_cast<const float4*>(k_sum + ((size_t)jj * Hkv + g) * D)[c4]
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
+  int32_t* out = block_idx + (size_t)h * nnz + row_ptr[i];
+  // the same for every head of the chunk, so block-uniform
+  if (!(kk > 0 && kk < nc && nc <= kRegCand)) {
+    if (kk >= nc) {                            // every earlier chunk is kept
+      for (int x = lane; x < nc; x += 64) out[x] = first + x;
+      if (lane == 0) out[nc] = i;
+    } else if (kk == 0) {
+      if (lane == 0) out[0] = i;
     }
-  };
-  uint64_t top = 0;
-  if (select) {
-    if (shared_kv) fetch(first);
-    for (int jb = first; jb < i; jb += 64) {
-      const int j = jb + lane;
-      float acc = 0.f;
-      if (shared_kv) {
-        __syncthreads();                       // the previous batch has been read
+    return;                                    // otherwise the general kernel writes this row
+  }
+  // the query side of the score: this head's summary, or (routing per KV head) the sum of the
+  // group's summaries in ascending head order (one wave forms it when the four heads share a group)
+  if (!(GROUPED && shared_kv) || wave == 0) {
+    for (int x = lane; x < D; x += 64) {
+      float acc = q_sum[((size_t)i * Hq + (GROUPED ? g * G : h)) * D + x];
+      if constexpr (GROUPED)
+        for (int hh = 1; hh < G; ++hh) acc += q_sum[((size_t)i * Hq + g * G + hh) * D + x];
+      qs[wave][x] = acc;
+    }
+  }
+
+  if (shared_kv) {
+    __syncthreads();                           // every head's query vector is in LDS
+    // lane = (candidate c of a block of 16, quarter qd); quarter qd holds float4 columns qd,
+    // qd + 4, ... of the candidate's K summary
+    constexpr int NV = D / 16;                 // float4 per lane per candidate
+    // routing per KV head: the four heads share one group, so one query vector serves all
+    constexpr int R = GROUPED ? 1 : kWaves;
+    const int c = lane >> 2, qd = lane & 3;
+    const int nblk = (nc + 15) >> 4;
+    for (int blk = wave; blk < nblk; blk += kWaves) {
+      float4 cur[NV];
+      const int j = min(first + 16 * blk + c, i - 1);   // rows past the end re-read the last one
+      const float4* kr = reinterpret_cast<const float4*>(k_sum + ((size_t)j * Hkv + g) * D);
 #pragma unroll
-        for (int p = 0; p < PER; ++p) {
-          const int x = threadIdx.x + p * kWaves * 64;
-          *reinterpret_cast<float4*>(&ks[x / (D / 4)][4 * (x % (D / 4))]) = pre[p];
-        }
-        __syncthreads();
-        if (jb + 64 < i) fetch(jb + 64);
-#pragma unroll 8
-        for (int x = 0; x < D / 4; ++x) {
-          const float4 kv = *reinterpret_cast<const float4*>(&ks[lane][4 * x]);
-          const float4 qv = *reinterpret_cast<const float4*>(&qs[wave][4 * x]);
-          acc = fmaf(qv.x, kv.x, acc);
-          acc = fmaf(qv.y, kv.y, acc);
-          acc = fmaf(qv.z, kv.z, acc);
-          acc = fmaf(qv.w, kv.w, acc);
-        }
-      } else if (j < i) {
-        const float4* kr = reinterpret_cast<const float4*>(k_sum + ((size_t)j * Hkv + g) * D);
-#pragma unroll 4
-        for (int x = 0; x < D / 4; ++x) {
-          const float4 kv = kr[x];
-          const float4 qv = *reinterpret_cast<const float4*>(&qs[wave][4 * x]);
-          acc = fmaf(qv.x, kv.x, acc);
-          acc = fmaf(qv.y, kv.y, acc);
-          acc = fmaf(qv.z, kv.z, acc);
-          acc = fmaf(qv.w, kv.w, acc);
+      for (int x = 0; x < NV; ++x) cur[x] = kr[qd + 4 * x];
+      asm volatile("" ::: "memory");           // re-read the query vectors from LDS each block
+      float acc[kWaves] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int x = 0; x < NV; ++x) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float4 qv = *reinterpret_cast<const float4*>(&qs[r][4 * (qd + 4 * x)]);
+          acc[r] = fmaf(qv.x, cur[x].x, acc[r]);
+          acc[r] = fmaf(qv.y, cur[x].y, acc[r]);
+          acc[r] = fmaf(qv.z, cur[x].z, acc[r]);
+          acc[r] = fmaf(qv.w, cur[x].w, acc[r]);
         }
       }
-      const uint64_t key = j < i ? rank_key(acc, j) : 0ull;
-      const uint64_t kth = shfl_u64(top, kk - 1);
-      if (__ballot(key > kth) == 0ull) continue;
-      top = merge_batch(top, key, lane);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        acc[r] += __shfl_xor(acc[r], 1);
+        acc[r] += __shfl_xor(acc[r], 2);
+      }
+      const float mine = qd == 0 ? acc[0] : qd == 1 ? acc[1] : qd == 2 ? acc[2] : acc[3];
+      if (16 * blk + c < nc && qd < R) sc[qd][16 * blk + c] = mine;
     }
+    __syncthreads();
+  } else {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int jb = 0; jb < nc; jb += 64) {
+      const int x0 = jb + lane;
+      if (x0 >= nc) continue;
+      const float4* kr = reinterpret_cast<const float4*>(k_sum + ((size_t)(first + x0) * Hkv + g) * D);
+      float acc = 0.f;
+#pragma unroll 4
+      for (int x = 0; x < D / 4; ++x) {
+        const float4 kv = kr[x];
+        const float4 qv = *reinterpret_cast<const float4*>(&qs[wave][4 * x]);
+        acc = fmaf(qv.x, kv.x, acc);
+        acc = fmaf(qv.y, kv.y, acc);
+        acc = fmaf(qv.z, kv.z, acc);
+        acc = fmaf(qv.w, kv.w, acc);
+      }
+      sc[wave][x0] = acc;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
-  int32_t* out = block_idx + (size_t)h * nnz + row_ptr[i];
-  if (select) {
-    const uint32_t jj = lane < kk ? (uint32_t)key_chunk(top) : 0xFFFFFFFFu;
-    const uint32_t srt = wave_sort_u32_asc(jj, lane);
-    if (lane < kk) out[lane] = (int32_t)srt;
-    if (lane == 0) out[kk] = i;
-  } else if (kk >= nc) {                       // every earlier chunk is kept
-    for (int x = lane; x < nc; x += 64) out[x] = first + x;
-    if (lane == 0) out[nc] = i;
-  } else if (kk == 0) {
-    if (lane == 0) out[0] = i;
-  }
-  // otherwise 64 < kk < nc: the general kernel writes this row
+  const int nb = (nc + 63) >> 6;
+  const float* row = sc[GROUPED && shared_kv ? 0 : wave];
+  uint32_t ob[kRegBatches];
+#pragma unroll
+  for (int b = 0; b < kRegBatches; ++b)
+    ob[b] = (b < nb && 64 * b + lane < nc) ? ordered_bits(row[64 * b + lane]) : 0u;
+  select_dispatch<1>(nb, ob, kk, first, lane, out);
+  if (lane == 0) out[kk] = i;
 }
 
-// General rows: more than 64 kept chunks out of a longer candidate list.
+// General rows: more candidates than the main kernel holds in registers.
 template <int D, bool GROUPED>
 __global__ __launch_bounds__(kWideThreads) void route_wide_kernel(
     const float* __restrict__ q_sum, const float* __restrict__ k_sum,
@@ -229,7 +235,7 @@ __global__ __launch_bounds__(kWideThreads) void route_wide_kernel(
   const int first = seq_chunk_start[seq_of_chunk(seq_chunk_start, B, i)];
   const int n = i - first;
   const int kk = row_ptr[i + 1] - row_ptr[i] - 1;
-  if (!(kk > kMaxTop && kk < n)) return;     // block-uniform
+  if (!(kk > 0 && kk < n && n > kRegCand)) return;   // block-uniform
   const int g = h / (Hq / Hkv);
   int npad = 1;
   while (npad < n) npad <<= 1;
@@ -301,7 +307,7 @@ __global__ __launch_bounds__(kWideThreads) void route_wide_kernel(
 template <int D, bool GROUPED>
 hipError_t launch_route_d(const Plan& p, const float* q_sum, const float* k_sum, const int32_t* row_ptr,
                           int64_t nnz, int32_t* block_idx, bool wide_rows, hipStream_t stream) {
-  dim3 grid(p.C, (p.Hq + kWaves - 1) / kWaves);
+  dim3 grid(p.C * ((p.Hq + kWaves - 1) / kWaves));
   hipLaunchKernelGGL((route_kernel<D, GROUPED>), grid, dim3(kWaves * 64), 0, stream, q_sum, k_sum, row_ptr,
                      p.seq_chunk_start, block_idx, p.B, p.C, p.Hq, p.Hkv, (long long)nnz);
   hipError_t err = hipGetLastError();

@@ -233,8 +233,8 @@ def test_dense_budget_equals_dense_attention():
     assert np.abs(g_o - dense).max() <= ATOL_BF16
 
 
-def test_wide_rows_use_general_selection():
-    # rows keep 70..100 of up to ~300 earlier chunks: more than one wave of keys
+def test_rows_keeping_more_than_a_wave_of_chunks():
+    # rows keep 70..100 of up to ~300 earlier chunks: more kept chunks than lanes in a wave
     w = small([SeqSpec(2400, ("uniform", 4, 12), 0, 4)], 4, 1, 64, "bf16", 23, "wide")
     tk = 70 + (np.arange(w.total_chunks) % 31).astype(np.int32)
     case = Case(w, topk=tk)
@@ -242,6 +242,18 @@ def test_wide_rows_use_general_selection():
     check_routing(case)
     check_routing(case, case.o_qs, case.o_ks)
     check_attention(case, heads=[0, 3], chunks=list(range(0, case.w.total_chunks, 7)))
+
+
+def test_rows_beyond_register_candidates_use_general_selection():
+    # one sequence of ~1250 short chunks: late rows have more than 1024 candidates, which the main
+    # routing kernel does not hold in registers, so the general sorting kernel selects them
+    w = small([SeqSpec(6200, ("uniform", 2, 8), 0, 0)], 4, 4, 64, "bf16", 25, "very_wide")
+    tk = np.where(np.arange(w.total_chunks) % 3 == 0, 40, 700).astype(np.int32)
+    case = Case(w, topk=tk)
+    assert w.total_chunks > 1100
+    check_routing(case)
+    check_routing(case, case.o_qs, case.o_ks)
+    check_attention(case, heads=[1], chunks=list(range(1030, case.w.total_chunks, 37)))
 
 
 def test_exact_ties_break_to_lower_index():
