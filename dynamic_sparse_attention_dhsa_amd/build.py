@@ -1,9 +1,11 @@
-"""Build the gfx950 HIP library ``libdhsa.so`` in place (hipcc, no JIT cache).
+"""Build the gfx950 HIP libraries in place (hipcc, no JIT cache).
 
-Every translation unit is compiled for gfx950 only, with packed fp32 vector
-instructions disabled in device code, then linked into one shared library
-next to this file.  ``python -m dynamic_sparse_attention_dhsa_amd.build``
-rebuilds it.
+``libdhsa.so``: every DHSA translation unit, compiled for gfx950 only with
+packed fp32 vector instructions disabled in device code, linked into one
+shared library next to this file.  ``libdhsa_calib.so``: the calibration
+kernels the benchmark measures the device's ceilings with (not part of the
+DHSA C ABI).  ``python -m dynamic_sparse_attention_dhsa_amd.build`` rebuilds
+both.
 """
 from __future__ import annotations
 
@@ -17,8 +19,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 LIB = os.path.join(PKG, "libdhsa.so")
+CALIB_LIB = os.path.join(PKG, "libdhsa_calib.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 SOURCES = ["api.cpp", "summarize.hip", "route.hip", "prefill_bf16.hip", "prefill_f32.hip"]
+CALIB_SOURCES = ["calib.hip"]
 ARCH = "gfx950"
 
 
@@ -51,18 +55,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES) + len(CALIB_SOURCES), 8)) as ex:
+        objs = list(ex.map(_compile, SOURCES + CALIB_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], CALIB_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CALIB_LIB}")
     return LIB
 
 

@@ -8,20 +8,22 @@
 // In the packed THD layout the tokens of chunk c form one contiguous block of
 // n_c rows of W = H * d elements, so the stage is a segmented column sum of a
 // row-major matrix: a pure HBM stream.  A workgroup owns one (chunk, block of
-// 512 columns); its four waves take every fourth row, each lane accumulates 8
-// adjacent columns in fp32 from 16-byte loads (bf16) with four rows in
-// flight, and the four partial sums are combined through LDS in a fixed order,
-// so results are reproducible run to run.  Q and K chunks go in one launch.
+// 512 columns); its eight waves take every eighth row, each lane accumulates 8
+// adjacent columns in fp32 from 16-byte loads (bf16) with eight rows in
+// flight, and the eight partial sums are combined through LDS in a fixed order,
+// so results are reproducible run to run.  Q and K chunks go in one launch,
+// column blocks fastest: the workgroups resident at any time read whole rows of
+// neighbouring chunks, not one column slice of every chunk.
 #include "dhsa_internal.hpp"
 
 namespace dhsa {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kColsPerLane = 8;
 constexpr int kColsPerBlock = 64 * kColsPerLane;  // 512
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 8;
 
 struct Vec8 { float v[8]; };
 
@@ -47,9 +49,9 @@ __global__ __launch_bounds__(kThreads) void summarize_kernel(
     const T* __restrict__ q, const T* __restrict__ k, float* __restrict__ q_sum,
     float* __restrict__ k_sum, const int32_t* __restrict__ cu_chunks, int Wq, int Wk, int nbq) {
   __shared__ float part[kWaves][kColsPerBlock];
-  const int c = blockIdx.x;
-  const bool is_q = (int)blockIdx.y < nbq;
-  const int cb = is_q ? blockIdx.y : blockIdx.y - nbq;
+  const int c = blockIdx.y;
+  const bool is_q = (int)blockIdx.x < nbq;
+  const int cb = is_q ? blockIdx.x : blockIdx.x - nbq;
   const int W = is_q ? Wq : Wk;
   const T* __restrict__ src = is_q ? q : k;
   float* __restrict__ dst = is_q ? q_sum : k_sum;
@@ -92,7 +94,9 @@ __global__ __launch_bounds__(kThreads) void summarize_kernel(
   for (int x = threadIdx.x; x < kColsPerBlock; x += kThreads) {
     const int cc = cb * kColsPerBlock + x;
     if (cc < W) {
-      float t = ((part[0][x] + part[1][x]) + part[2][x]) + part[3][x];
+      float t = part[0][x];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) t += part[w][x];
       dst[(size_t)c * W + cc] = t * inv_norm;
     }
   }
@@ -106,7 +110,7 @@ hipError_t launch_summarize(const Plan& p, const void* q, const void* k, float* 
   const int Wq = p.Hq * p.d, Wk = p.Hkv * p.d;
   const int nbq = (Wq + kColsPerBlock - 1) / kColsPerBlock;
   const int nbk = (Wk + kColsPerBlock - 1) / kColsPerBlock;
-  dim3 grid(p.C, nbq + nbk);
+  dim3 grid(nbq + nbk, p.C);
   if (p.dtype == 1) {
     hipLaunchKernelGGL(summarize_kernel<uint16_t>, grid, dim3(kThreads), 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k, q_sum, k_sum, p.cu_chunks, Wq, Wk, nbq);

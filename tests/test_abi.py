@@ -36,6 +36,28 @@ def test_library_exports_every_declared_symbol():
     assert lib.dhsa_status_str(5).decode().startswith("DHSA_ERR_UNSUPPORTED")
 
 
+CALIB_HEADER = os.path.join(ROOT, "include", "dhsa_calib.h")
+
+
+def test_calibration_library_exports_and_checks_arguments():
+    """libdhsa_calib.so (measurement only) exports what dhsa_calib.h declares and refuses bad
+    arguments before launching anything (hipErrorInvalidValue = 1)."""
+    from dynamic_sparse_attention_dhsa_amd.build import CALIB_LIB
+    text = open(CALIB_HEADER).read()
+    names = sorted(set(re.findall(r"^int\s+(dhsa_calib_\w+)\s*\(", text, flags=re.M)))
+    assert names == ["dhsa_calib_mfma_bf16", "dhsa_calib_read"]
+    cal = ctypes.CDLL(CALIB_LIB)
+    for n in names:
+        assert hasattr(cal, n), n
+    vp = ctypes.c_void_p
+    cal.dhsa_calib_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
+    cal.dhsa_calib_read.argtypes = [vp, ctypes.c_size_t, ctypes.c_int, vp, vp]
+    assert cal.dhsa_calib_mfma_bf16(0, 10, vp(FAKE), None) == 1
+    assert cal.dhsa_calib_mfma_bf16(4, 10, None, None) == 1
+    assert cal.dhsa_calib_read(vp(FAKE), 24, 4, vp(FAKE), None) == 1      # not a multiple of 16
+    assert cal.dhsa_calib_read(None, 32, 4, vp(FAKE), None) == 1
+
+
 class Mirror:
     def __init__(self, cs, cc, sc, Hq=4, Hkv=2, d=128, dtype=1, T=None, C=None, B=None):
         self.cs, self.cc, self.sc = (np.ascontiguousarray(x, np.int32) for x in (cs, cc, sc))
