@@ -367,6 +367,99 @@ def pin_grouped_routing(O):
             assert np.array_equal(grouped[1][h], single[1][g]), (g, h)
 
 
+# ----------------------------------------------------------------------------- online chunking rule (our design)
+
+def _num(x):
+    x = str(x).strip()
+    neg = x.startswith("-")
+    x = x.lstrip("-")
+    v = math.sqrt(float(Fraction(x[5:-1]))) if x.startswith("sqrt(") else float(Fraction(x))
+    return -v if neg else v
+
+
+def pin_chunking_golden(O):
+    g = json.load(open(os.path.join(GOLDEN, "g4_chunk_boundaries.json")))
+    k = np.array(g["k"], np.float32)
+    sim = O.adjacent_similarity(k, g["cu_seqlens"])
+    want = np.array([_num(x) for x in g["expected_sim"]], np.float64).astype(np.float32)
+    assert sim.dtype == np.float32 and np.array_equal(sim, want), (sim, want)
+    for case in g["cases"]:
+        cc, sc = O.chunk_boundaries(want, g["cu_seqlens"], case["lo"], case["hi"], case["tau"])
+        assert cc.tolist() == case["cu_chunks"] and sc.tolist() == case["seq_chunk_start"], (case, cc, sc)
+
+
+def pin_chunking_closed_forms(O):
+    rng = np.random.default_rng(11)
+    # equal rows: similarity 1 everywhere, so chunks are hi long (the last one what remains)
+    row = rng.standard_normal((1, 2, 8)).astype(np.float32)
+    k = np.repeat(row, 23, axis=0)
+    sim = O.adjacent_similarity(k, [0, 23])
+    assert np.allclose(sim, 1.0, atol=1e-6)
+    cc, sc = O.chunk_boundaries(sim, [0, 23], 2, 5, 0.9)
+    assert cc.tolist() == [0, 5, 10, 15, 20, 23] and sc.tolist() == [0, 5]
+    # rows alternating between two orthogonal directions: similarity 0, so chunks are lo long
+    e = np.zeros((2, 2, 8), np.float32)
+    e[0, 0, 0] = 3.0
+    e[1, 1, 5] = -2.0
+    k = np.concatenate([e] * 9, axis=0)[:17]
+    sim = O.adjacent_similarity(k, [0, 17])
+    assert sim[0] == 1.0 and np.all(sim[1:] == 0.0)
+    cc, _ = O.chunk_boundaries(sim, [0, 17], 3, 7, 0.5)
+    assert cc.tolist() == [0, 3, 6, 9, 12, 15, 17]
+    # lo == hi: fixed-length chunks whatever the similarity
+    sim = rng.uniform(-1, 1, 40).astype(np.float32)
+    cc, sc = O.chunk_boundaries(sim, [0, 13, 13, 40], 4, 4, 0.0)
+    assert cc.tolist() == [0, 4, 8, 12, 13, 17, 21, 25, 29, 33, 37, 40] and sc.tolist() == [0, 4, 4, 11]
+
+
+def pin_chunking_rule_invariants(O):
+    """Property check of the greedy cut, independent of how it is computed: the chunks tile every
+    sequence, lengths respect [lo, hi] (the last chunk of a sequence may be shorter), no position a
+    chunk could have been cut at earlier has a drop, and a chunk shorter than its limit ends at a drop."""
+    rng = np.random.default_rng(12)
+    for trial in range(200):
+        lens = rng.integers(0, 40, size=rng.integers(1, 4))
+        cs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+        sim = rng.choice(np.array([-0.5, 0.2, 0.5, 0.9, 1.0], np.float32), size=int(cs[-1]))
+        lo = int(rng.integers(1, 6))
+        hi = int(rng.integers(lo, 12))
+        tau = float(rng.choice([0.2, 0.5, 0.95]))
+        cc, sc = O.chunk_boundaries(sim, cs, lo, hi, tau)
+        assert sc.size == cs.size and sc[0] == 0 and cc[0] == 0 and cc[-1] == cs[-1]
+        for b in range(cs.size - 1):
+            bounds = cc[sc[b]:sc[b + 1] + 1]
+            assert bounds[0] == cs[b] and bounds[-1] == cs[b + 1]
+            for c0, c1 in zip(bounds[:-1], bounds[1:]):
+                n = c1 - c0
+                assert 1 <= n <= hi
+                last = c1 == cs[b + 1]
+                if not last:
+                    assert n >= lo
+                assert all(sim[t] >= np.float32(tau) for t in range(c0 + lo, c1))
+                if n < hi and not last:
+                    assert sim[c1] < np.float32(tau)
+
+
+def pin_similarity_library(O):
+    """sim against torch's cosine_similarity in float64 on random keys, two sequences."""
+    rng = np.random.default_rng(13)
+    k = rng.standard_normal((50, 3, 16)).astype(np.float32)
+    cs = [0, 21, 50]
+    sim = O.adjacent_similarity(k, cs)
+    rows = torch.from_numpy(k.reshape(50, -1).astype(np.float64))
+    ref = torch.nn.functional.cosine_similarity(rows[:-1], rows[1:], dim=1).numpy()
+    for t in range(50):
+        if t in (0, 21):
+            assert sim[t] == 1.0
+        else:
+            assert abs(float(sim[t]) - ref[t - 1]) <= 1e-6, t
+    # positive per-row scale leaves every similarity unchanged
+    scale = rng.uniform(0.1, 10.0, size=(50, 1, 1)).astype(np.float64)
+    sim2 = O.adjacent_similarity(k.astype(np.float64) * scale, cs)
+    assert np.allclose(sim2, sim, atol=1e-6)
+
+
 ALL_PINS = [pin_golden, pin_summary_closed_forms, pin_scores_bruteforce, pin_topk_bruteforce,
             pin_kept_invariants, pin_dense_special_case, pin_token_level_bruteforce, pin_row_sum_and_lse,
-            pin_causality, pin_gqa_and_permutation, pin_ragged_equals_separate, pin_grouped_routing]
+            pin_causality, pin_gqa_and_permutation, pin_ragged_equals_separate, pin_grouped_routing,
+            pin_chunking_golden, pin_chunking_closed_forms, pin_chunking_rule_invariants, pin_similarity_library]

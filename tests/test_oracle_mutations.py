@@ -1,8 +1,9 @@
 """Plant plausible mistakes in copies of the CPU oracle; each copy must fail at least one pin.
 
-The mistakes are textual edits of oracle/dhsa_oracle.py applied to an
-in-memory copy (the oracle on disk is never touched).  Each edit must match
-exactly once, so the list stays in step with the oracle's source.
+The mistakes are textual edits of oracle/dhsa_oracle.py or oracle/chunking_oracle.py applied to an
+in-memory copy (the oracle on disk is never touched); the mutant module holds both files' functions,
+one of them edited, so a pin of the other file cannot "catch" it by a missing name.  Each edit must
+match exactly once, so the lists stay in step with the oracle's source.
 """
 import os
 import types
@@ -11,7 +12,9 @@ import pytest
 
 import oracle_pins
 
-SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "dhsa_oracle.py")
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+SRC = os.path.join(ORACLE_DIR, "dhsa_oracle.py")
+CHUNK_SRC = os.path.join(ORACLE_DIR, "chunking_oracle.py")
 
 MUTATIONS = {
     "plain_mean": ("out[c] = mean * np.sqrt(n)", "out[c] = mean"),
@@ -52,18 +55,40 @@ MUTATIONS = {
 }
 
 
-def _mutant(old, new):
-    with open(SRC) as f:
-        src = f.read()
-    assert src.count(old) == 1, f"mutation anchor not found exactly once: {old!r}"
-    mod = types.ModuleType("dhsa_oracle_mutant")
-    exec(compile(src.replace(old, new), "dhsa_oracle_mutant", "exec"), mod.__dict__)
+CHUNK_MUTATIONS = {
+    "chunk_lo_off_by_one": ("for t in range(c0 + lo, end):", "for t in range(c0 + lo + 1, end):"),
+    "chunk_cut_at_equal": ("if sim[t] < tau32:", "if sim[t] <= tau32:"),
+    "chunk_hi_exclusive": ("end = min(c0 + hi, e)", "end = min(c0 + hi - 1, e)"),
+    "chunk_cut_after_drop": ("                    cut = t\n", "                    cut = t + 1\n"),
+    "sim_unnormalised": ("sim[t] = float(np.dot(a, c)) / np.sqrt(na * nc)", "sim[t] = float(np.dot(a, c))"),
+    "sim_across_sequences": ("for t in range(int(cs[b]) + 1, int(cs[b + 1])):",
+                             "for t in range(max(int(cs[b]), 1), int(cs[b + 1])):"),
+    "sim_zero_rows_compared": ("if na > 0.0 and nc > 0.0:", "if na > 0.0 or nc > 0.0:"),
+    "sim_first_head_only": ("rows = k.reshape(T, -1).astype(np.float64)", "rows = k[:, 0, :].astype(np.float64)"),
+}
+
+
+def _mutant(old, new, chunking=False):
+    srcs = {}
+    for path in (SRC, CHUNK_SRC):
+        with open(path) as f:
+            srcs[path] = f.read()
+    target = CHUNK_SRC if chunking else SRC
+    assert srcs[target].count(old) == 1, f"mutation anchor not found exactly once: {old!r}"
+    srcs[target] = srcs[target].replace(old, new)
+    mod = types.ModuleType("oracle_mutant")
+    for path, src in srcs.items():
+        exec(compile(src, os.path.basename(path), "exec"), mod.__dict__)
     return mod
 
 
-@pytest.mark.parametrize("name", sorted(MUTATIONS))
+ALL = {**{n: (m, False) for n, m in MUTATIONS.items()}, **{n: (m, True) for n, m in CHUNK_MUTATIONS.items()}}
+
+
+@pytest.mark.parametrize("name", sorted(ALL))
 def test_mutant_is_caught(name):
-    mod = _mutant(*MUTATIONS[name])
+    (old, new), chunking = ALL[name]
+    mod = _mutant(old, new, chunking)
     caught = []
     for pin in oracle_pins.ALL_PINS:
         try:
