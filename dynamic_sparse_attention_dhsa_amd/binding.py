@@ -26,7 +26,8 @@ STATUS_NAMES = {0: "DHSA_OK", 1: "DHSA_ERR_NULL_ARG", 2: "DHSA_ERR_BAD_SHAPE", 3
 
 # every entry point declared in include/dhsa.h
 EXPORTS = ("dhsa_abi_version", "dhsa_status_str", "dhsa_validate_layout", "dhsa_route_plan",
-           "dhsa_chunk_summarize", "dhsa_route", "dhsa_route_grouped", "dhsa_sparse_prefill")
+           "dhsa_chunk_summarize", "dhsa_route", "dhsa_route_grouped", "dhsa_sparse_prefill",
+           "dhsa_adjacent_similarity", "dhsa_chunk_boundaries")
 
 
 class DhsaError(RuntimeError):
@@ -72,6 +73,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         getattr(lib, name).argtypes = [lp, vp, vp, vp, vp, i64, vp, vp]
     lib.dhsa_sparse_prefill.restype = i32
     lib.dhsa_sparse_prefill.argtypes = [lp, vp, vp, vp, vp, vp, i64, vp, ctypes.c_float, vp, vp, vp]
+    lib.dhsa_adjacent_similarity.restype = i32
+    lib.dhsa_adjacent_similarity.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, ctypes.c_float, vp, vp, vp]
+    lib.dhsa_chunk_boundaries.restype = i32
+    lib.dhsa_chunk_boundaries.argtypes = [i32, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp]
     if lib.dhsa_abi_version() != 1:
         raise RuntimeError("libdhsa.so ABI version mismatch")
     _LIB = lib
@@ -232,3 +237,78 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens, cu_ch
     out, lse = res if return_lse else (res, None)
     return dict(out=out, lse=lse, q_sum=q_sum, k_sum=k_sum, row_ptr=plan.h_row_ptr, block_idx=block_idx,
                 layout=layout, plan=plan)
+
+
+# ----------------------------------------------------------------------------- online chunking (own rule)
+
+class SeqLayout:
+    """Token offsets of a batch for the chunking calls: device copy plus host mirror (built once)."""
+
+    def __init__(self, cu_seqlens, device="cuda"):
+        self.h_cu_seqlens = _host_i32(cu_seqlens)
+        self.d_cu_seqlens = torch.from_numpy(self.h_cu_seqlens).to(torch.device(device))
+        self.num_seqs = self.h_cu_seqlens.size - 1
+        self.total_tokens = int(self.h_cu_seqlens[-1])
+
+
+def _seq_layout(cu_seqlens, device) -> SeqLayout:
+    return cu_seqlens if isinstance(cu_seqlens, SeqLayout) else SeqLayout(cu_seqlens, device)
+
+
+def adjacent_similarity(k: torch.Tensor, cu_seqlens, tau: float, sim: Optional[torch.Tensor] = None,
+                        cut_bits: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """dhsa_adjacent_similarity: sim float32 [T] (cosine of adjacent key rows over all KV heads, 1 at
+    sequence starts and zero rows) and cut_bits int64 [ceil(T/64)] (bit t set when sim[t] < tau).
+    ``cu_seqlens``: a SeqLayout, or host offsets (copied to the device on each call)."""
+    if not k.is_cuda or k.dim() != 3 or not k.is_contiguous():
+        raise DhsaError(2, "k", "expected a contiguous GPU tensor [T, Hkv, d]")
+    if k.dtype == torch.bfloat16:
+        code = DHSA_BF16
+    elif k.dtype == torch.float32:
+        code = DHSA_F32
+    else:
+        raise DhsaError(5, "k", f"unsupported dtype {k.dtype}")
+    sl = _seq_layout(cu_seqlens, k.device)
+    T = k.shape[0]
+    if sim is None:
+        sim = torch.empty(T, dtype=torch.float32, device=k.device)
+    if cut_bits is None:
+        cut_bits = torch.empty((T + 63) // 64, dtype=torch.int64, device=k.device)
+    if sim.numel() < T or cut_bits.numel() < (T + 63) // 64:
+        raise DhsaError(2, "sim/cut_bits", "output buffers too small")
+    _check(load_library().dhsa_adjacent_similarity(sl.num_seqs, T, k.shape[1], k.shape[2], code,
+                                                   _ptr(sl.d_cu_seqlens), sl.h_cu_seqlens.ctypes.data, _ptr(k),
+                                                   float(tau), _ptr(sim), _ptr(cut_bits), _stream()),
+           "dhsa_adjacent_similarity")
+    return sim, cut_bits
+
+
+def chunk_boundaries(cut_bits: torch.Tensor, cu_seqlens, lo: int, hi: int,
+                     out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None
+                     ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """dhsa_chunk_boundaries: device cu_chunks int32 [T+1] (entries 0..C valid), seq_chunk_start
+    int32 [B+1] and num_chunks int32 [1] (``out`` supplies them preallocated)."""
+    if not cut_bits.is_cuda or cut_bits.dtype != torch.int64:
+        raise DhsaError(2, "cut_bits", "expected an int64 GPU tensor")
+    sl = _seq_layout(cu_seqlens, cut_bits.device)
+    T = sl.total_tokens
+    if cut_bits.numel() != (T + 63) // 64:
+        raise DhsaError(2, "cut_bits", f"expected {(T + 63) // 64} words")
+    if out is None:
+        out = (torch.empty(T + 1, dtype=torch.int32, device=cut_bits.device),
+               torch.empty(sl.num_seqs + 1, dtype=torch.int32, device=cut_bits.device),
+               torch.empty(1, dtype=torch.int32, device=cut_bits.device))
+    cu_chunks, scs, nch = out
+    _check(load_library().dhsa_chunk_boundaries(sl.num_seqs, T, _ptr(sl.d_cu_seqlens), sl.h_cu_seqlens.ctypes.data,
+                                                _ptr(cut_bits), int(lo), int(hi), _ptr(cu_chunks), _ptr(scs),
+                                                _ptr(nch), _stream()), "dhsa_chunk_boundaries")
+    return cu_chunks, scs, nch
+
+
+def online_chunks(k: torch.Tensor, cu_seqlens, lo: int, hi: int, tau: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Both chunking steps, then the host copies a Layout needs: (cu_chunks [C+1], seq_chunk_start [B+1])."""
+    sl = _seq_layout(cu_seqlens, k.device)
+    _, bits = adjacent_similarity(k, sl, tau)
+    cu_chunks, scs, nch = chunk_boundaries(bits, sl, lo, hi)
+    C = int(nch.cpu().item())
+    return cu_chunks[:C + 1].cpu().numpy(), scs.cpu().numpy()

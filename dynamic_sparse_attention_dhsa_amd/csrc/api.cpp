@@ -76,6 +76,17 @@ dhsa_status check_row_ptr(const dhsa_layout* L, const int32_t* h_row_ptr, int64_
 
 dhsa_status launched(hipError_t e) { return e == hipSuccess ? DHSA_OK : DHSA_ERR_LAUNCH; }
 
+// Token offsets of a batch (host mirror): start at 0, monotone, end at T.
+dhsa_status check_seqlens(int32_t B, int32_t T, const int32_t* cu_seqlens, const int32_t* h_cu_seqlens) {
+  if (B < 0 || T < 0) return DHSA_ERR_BAD_SHAPE;
+  if (cu_seqlens == nullptr || h_cu_seqlens == nullptr) return DHSA_ERR_NULL_ARG;
+  if (h_cu_seqlens[0] != 0 || h_cu_seqlens[B] != T) return DHSA_ERR_BAD_LAYOUT;
+  for (int32_t b = 0; b < B; ++b)
+    if (h_cu_seqlens[b + 1] < h_cu_seqlens[b]) return DHSA_ERR_BAD_LAYOUT;
+  return DHSA_OK;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -178,6 +189,42 @@ dhsa_status dhsa_sparse_prefill(const dhsa_layout* layout, const void* q, const 
   if (p.dtype == DHSA_BF16)
     return launched(dhsa::launch_prefill_bf16(p, q, k, v, row_ptr, nnz, block_idx, softmax_scale, out, lse, s));
   return launched(dhsa::launch_prefill_f32(p, q, k, v, row_ptr, nnz, block_idx, softmax_scale, out, lse, s));
+}
+
+
+dhsa_status dhsa_adjacent_similarity(int32_t num_seqs, int32_t total_tokens, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t dtype, const int32_t* cu_seqlens,
+                                     const int32_t* h_cu_seqlens, const void* k, float tau, float* sim,
+                                     uint64_t* cut_bits, void* stream) {
+  dhsa_status st = check_seqlens(num_seqs, total_tokens, cu_seqlens, h_cu_seqlens);
+  if (st != DHSA_OK) return st;
+  if (num_kv_heads < 1 || head_dim < 1 || (int64_t)num_kv_heads * head_dim > INT32_MAX / 4) return DHSA_ERR_BAD_SHAPE;
+  if (dtype != DHSA_F32 && dtype != DHSA_BF16) return DHSA_ERR_UNSUPPORTED;
+  const int32_t W = num_kv_heads * head_dim;
+  if (W % (dtype == DHSA_BF16 ? 8 : 4) != 0) return DHSA_ERR_UNSUPPORTED;
+  if (W / (dtype == DHSA_BF16 ? 8 : 4) > dhsa::kSimMaxPieces) return DHSA_ERR_UNSUPPORTED;
+  if (!isfinite(tau)) return DHSA_ERR_BAD_SHAPE;
+  if (total_tokens == 0) return DHSA_OK;
+  if (k == nullptr || sim == nullptr || cut_bits == nullptr) return DHSA_ERR_NULL_ARG;
+  return launched(dhsa::launch_adjacent_similarity(num_seqs, total_tokens, W, dtype, cu_seqlens, k, tau, sim,
+                                                   cut_bits, (hipStream_t)stream));
+}
+
+dhsa_status dhsa_chunk_boundaries(int32_t num_seqs, int32_t total_tokens, const int32_t* cu_seqlens,
+                                  const int32_t* h_cu_seqlens, const uint64_t* cut_bits, int32_t lo, int32_t hi,
+                                  int32_t* cu_chunks, int32_t* seq_chunk_start, int32_t* num_chunks,
+                                  void* stream) {
+  dhsa_status st = check_seqlens(num_seqs, total_tokens, cu_seqlens, h_cu_seqlens);
+  if (st != DHSA_OK) return st;
+  if (lo < 1 || hi < lo) return DHSA_ERR_BAD_SHAPE;
+  if (cu_chunks == nullptr || seq_chunk_start == nullptr || num_chunks == nullptr) return DHSA_ERR_NULL_ARG;
+  if (total_tokens > 0 && cut_bits == nullptr) return DHSA_ERR_NULL_ARG;
+  // Limits past the longest sequence change nothing; clamping keeps c0 + hi inside int range.
+  const int32_t cap = total_tokens > 0 ? total_tokens : 1;
+  const int32_t hi_c = hi < cap ? hi : cap;
+  const int32_t lo_c = lo < hi_c ? lo : hi_c;
+  return launched(dhsa::launch_chunk_walk(num_seqs, total_tokens, cu_seqlens, cut_bits, lo_c, hi_c, cu_chunks,
+                                          seq_chunk_start, num_chunks, (hipStream_t)stream));
 }
 
 }  // extern "C"

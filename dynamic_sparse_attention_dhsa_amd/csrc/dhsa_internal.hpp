@@ -39,6 +39,14 @@ hipError_t launch_prefill_f32(const Plan& p, const void* q, const void* k, const
                               const int32_t* row_ptr, int64_t nnz, const int32_t* block_idx,
                               float softmax_scale, void* out, float* lse, hipStream_t stream);
 
+// Online chunking (this library's own boundary rule).  A key row is read in at most kSimMaxPieces
+// 16-byte pieces (8 per lane).
+constexpr int kSimMaxPieces = 512;
+hipError_t launch_adjacent_similarity(int B, int ntok, int W, int dtype, const int32_t* cu_seqlens, const void* k,
+                                      float tau, float* sim, uint64_t* cut_bits, hipStream_t stream);
+hipError_t launch_chunk_walk(int B, int ntok, const int32_t* cu_seqlens, const uint64_t* cut_bits, int lo, int hi,
+                             int32_t* cu_chunks, int32_t* seq_chunk_start, int32_t* num_chunks, hipStream_t stream);
+
 // Device helpers ----------------------------------------------------------------------------
 
 // Index of the sequence containing chunk c: the last b with seq_chunk_start[b] <= c.

@@ -156,6 +156,51 @@ dhsa_status dhsa_sparse_prefill(const dhsa_layout* layout, const void* q, const 
                                 int64_t nnz, const int32_t* block_idx, float softmax_scale,
                                 void* out, float* lse, void* stream);
 
+/* ---- Online chunking (this library's own rule, an extension: the pages
+ * claim online variable-length chunking as the step before the summaries -
+ * "Long-Context Modeling with Dynamic Hierarchical Sparse Attention for
+ * On-Device LLMs", Abstract and Innovation; ICML 2026 page, Abstract - but
+ * state no rule).  The rule: a cut may fall between adjacent tokens whose key
+ * rows point in different directions, and chunks hold between lo and hi
+ * tokens.  Its output feeds dhsa_layout (copy cu_chunks / seq_chunk_start to
+ * the host for the mirrors). */
+
+/* Step 1, adjacent key similarity.  For every token t of sequence b:
+ *   sim[t] = cos(k[t-1, :, :], k[t, :, :])    over all KV heads of the two rows
+ *            (fp32 accumulation), or 1 when t is the first token of its
+ *            sequence or either row is all zeros;
+ *   bit (t mod 64) of cut_bits[t / 64] = (sim[t] < tau).
+ *   cu_seqlens    device [B+1] token offsets; h_cu_seqlens its host mirror
+ *                 (required: validated like dhsa_layout's)
+ *   k             device [T, Hkv, d], dtype DHSA_BF16 or DHSA_F32, 16-byte aligned;
+ *                 Hkv * d must be a multiple of 8 (bf16) or 4 (fp32) and at most
+ *                 4096 (bf16) or 2048 (fp32): a row is 16-byte loads, at most 8 per lane
+ *   tau           finite cut threshold
+ *   sim           device float[T], written completely
+ *   cut_bits      device uint64[ceil(T / 64)], written completely (bits past T are 0)
+ * T == 0 launches nothing.  Errors as for the stage calls. */
+dhsa_status dhsa_adjacent_similarity(int32_t num_seqs, int32_t total_tokens, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t dtype, const int32_t* cu_seqlens,
+                                     const int32_t* h_cu_seqlens, const void* k, float tau, float* sim,
+                                     uint64_t* cut_bits, void* stream);
+
+/* Step 2, greedy cut.  Per sequence, from its first token c0: the chunk ends at
+ * the first t in [c0 + lo, min(c0 + hi, end of sequence)) whose cut bit is set,
+ * else at min(c0 + hi, end); the next chunk starts there.  So every chunk but a
+ * sequence's last holds between lo and hi tokens, the last at most hi.
+ *   cut_bits         device uint64[ceil(T / 64)] from dhsa_adjacent_similarity
+ *   lo, hi           1 <= lo <= hi
+ *   cu_chunks        device int32[T + 1] (capacity): entries 0..C written,
+ *                    cu_chunks[0] = 0, cu_chunks[C] = T
+ *   seq_chunk_start  device int32[B + 1], written
+ *   num_chunks       device int32[1]: C
+ * One workgroup walks the sequences in order (the cut is sequential by nature);
+ * it stages the bitmap in 64 KB of LDS at a time. */
+dhsa_status dhsa_chunk_boundaries(int32_t num_seqs, int32_t total_tokens, const int32_t* cu_seqlens,
+                                  const int32_t* h_cu_seqlens, const uint64_t* cut_bits, int32_t lo, int32_t hi,
+                                  int32_t* cu_chunks, int32_t* seq_chunk_start, int32_t* num_chunks,
+                                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

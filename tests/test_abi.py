@@ -180,3 +180,37 @@ def test_python_binding_refuses_cpu_tensors():
     lay.dtype, lay.total_tokens, lay.head_dim = torch.bfloat16, 4, 64
     with pytest.raises(Bd.DhsaError):
         lay._check_tensor(torch.zeros(4, 1, 64, dtype=torch.bfloat16), 1, "q")
+
+
+def test_chunking_calls_reject_before_launch():
+    lib = Bd.load_library()
+    vp = ctypes.c_void_p
+    cs = np.array([0, 10, 10, 25], np.int32)
+    good = dict(B=3, T=25)
+
+    def sim(B=3, T=25, hkv=2, d=64, dt=1, h_cs=cs, tau=0.5, k=FAKE, out=FAKE, bits=FAKE):
+        return lib.dhsa_adjacent_similarity(B, T, hkv, d, dt, vp(FAKE), h_cs.ctypes.data if h_cs is not None else None,
+                                            vp(k) if k else None, tau, vp(out) if out else None,
+                                            vp(bits) if bits else None, None)
+
+    assert sim(T=24) == LAYOUT                       # mirror does not end at T
+    assert sim(h_cs=np.array([0, 10, 9, 25], np.int32)) == LAYOUT
+    assert sim(h_cs=None) == NULL
+    assert sim(dt=7) == UNSUP
+    assert sim(hkv=1, d=12) == UNSUP                 # row of 12 bf16 is not a whole number of 16-byte loads
+    assert sim(hkv=64, d=128) == UNSUP               # a row of 8192 bf16 is more than 8 loads per lane
+    assert sim(tau=float("nan")) == SHAPE
+    assert sim(k=0) == NULL
+    assert sim(B=0, T=0, h_cs=np.array([0], np.int32), k=0, out=0, bits=0) == OK   # empty: nothing launched
+
+    def walk(lo=2, hi=8, h_cs=cs, T=25, bits=FAKE, out=FAKE):
+        return lib.dhsa_chunk_boundaries(3, T, vp(FAKE), h_cs.ctypes.data if h_cs is not None else None,
+                                         vp(bits) if bits else None, lo, hi, vp(out) if out else None,
+                                         vp(FAKE), vp(FAKE), None)
+
+    assert walk(lo=0) == SHAPE
+    assert walk(lo=5, hi=4) == SHAPE
+    assert walk(T=26) == LAYOUT
+    assert walk(h_cs=None) == NULL
+    assert walk(bits=0) == NULL
+    assert walk(out=0) == NULL
