@@ -1,5 +1,5 @@
-"""CPU oracle for DHSA chunk-routed sparse causal prefill, and for this project's online
-chunk-boundary rule (test infrastructure only).
+"""CPU oracle for DHSA chunk-routed sparse causal prefill, for this project's online
+chunk-boundary rule and for decode against the kept structure (test infrastructure only).
 
 Only tests/, ``__graft_entry__.smoke()`` and bench.py's ``cpu_baseline`` leg
 import this package.  It shares no code with the HIP path.
@@ -9,3 +9,4 @@ from .dhsa_oracle import (attend, chunk_scores, chunk_sequence, chunk_summaries,
                           route_grouped, route_plan, select_key_chunks, token_importance,
                           validate_layout)
 from .chunking_oracle import adjacent_similarity, chunk_boundaries  # noqa: F401,E402
+from .decode_oracle import decode_sequence  # noqa: F401,E402

@@ -459,7 +459,90 @@ def pin_similarity_library(O):
     assert np.allclose(sim2, sim, atol=1e-6)
 
 
+# ----------------------------------------------------------------------------- decode against the kept structure
+
+def _decode_inputs(seed, T=90, Hq=4, Hkv=2, d=8, shift_every=None):
+    """Random q/k/v; keys drift within stretches so the cut rule sees both high and low similarity."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((T, Hq, d))
+    base = rng.standard_normal((T // 7 + 1, Hkv, d))
+    k = np.repeat(base, 7, axis=0)[:T] + 0.4 * rng.standard_normal((T, Hkv, d))
+    v = rng.standard_normal((T, Hkv, d))
+    return q, k, v
+
+
+def pin_decode_cuts_match_offline(O):
+    for seed, (lo, hi, tau) in enumerate([(2, 9, 0.6), (1, 4, 0.9), (5, 5, 0.0), (3, 40, 0.3)]):
+        q, k, v = _decode_inputs(100 + seed)
+        _, starts, _ = O.decode_sequence(q, k, v, lo, hi, tau, 2, 0.3, first_output=len(q) - 1)
+        cc, _ = O.chunk_boundaries(O.adjacent_similarity(k, [0, len(q)]), [0, len(q)], lo, hi, tau)
+        assert starts + [len(q)] == cc.tolist(), (starts, cc)
+
+
+def pin_decode_chunk_end_equals_prefill(O):
+    """At the last token of every chunk the open summary is the chunk's prefill summary, so the decode
+    output equals the prefill oracle's output at that token (same boundaries, same budget)."""
+    for grouped in (False, True):
+        q, k, v = _decode_inputs(110 + grouped)
+        T = len(q)
+        lo, hi, tau, topk, scale = 3, 12, 0.6, 2, 0.37
+        out, starts, kept = O.decode_sequence(q, k, v, lo, hi, tau, topk, scale, grouped=grouped)
+        cu = np.array(starts + [T], np.int32)
+        scs = np.array([0, len(starts)], np.int32)
+        tk = np.full(len(starts), topk, np.int32)
+        qs = O.chunk_summaries(q, cu)
+        ks = O.chunk_summaries(k, cu)
+        rp, bi, _ = (O.route_grouped if grouped else O.route)(qs, ks, scs, tk)
+        o_pre, _ = O.attend(q, k, v, cu, rp, bi, scale)
+        for i in range(len(starts)):
+            t = int(cu[i + 1]) - 1
+            for h in range(q.shape[1]):
+                assert kept[t][h] == bi[h, rp[i]:rp[i + 1] - 1].tolist(), (t, h)
+            assert np.abs(out[t] - o_pre[t]).max() < 1e-10, t
+
+
+def pin_decode_dense_equals_causal_attention(O):
+    q, k, v = _decode_inputs(120, T=50)
+    T, Hq, d = q.shape
+    G = Hq // k.shape[1]
+    out, _, _ = O.decode_sequence(q, k, v, 2, 6, 0.5, 10 ** 6, 0.41)
+    qt = torch.from_numpy(q).permute(1, 0, 2)
+    kt = torch.from_numpy(np.repeat(k, G, axis=1)).permute(1, 0, 2)
+    vt = torch.from_numpy(np.repeat(v, G, axis=1)).permute(1, 0, 2)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=0.41)
+    assert np.abs(out - ref.permute(1, 0, 2).numpy()).max() < 1e-10
+
+
+def pin_decode_first_output_and_groups(O):
+    """Outputs do not depend on where output starts; grouped routing with one head per group is per-head."""
+    q, k, v = _decode_inputs(130, Hq=2, Hkv=2)
+    a, sa, ka = O.decode_sequence(q, k, v, 2, 9, 0.6, 2, 0.3)
+    b, sb, kb = O.decode_sequence(q, k, v, 2, 9, 0.6, 2, 0.3, first_output=40)
+    assert sa == sb and np.array_equal(a[40:], b) and ka[40:] == kb
+    c, sc, kc = O.decode_sequence(q, k, v, 2, 9, 0.6, 2, 0.3, grouped=True)
+    assert sc == sa and kc == ka and np.array_equal(c, a)
+
+
+def pin_decode_ties_to_lower_index(O):
+    """Identical key rows: no cut before hi, every closed chunk has the same summary, every score ties
+    exactly, so the kept chunks are the lowest indices."""
+    rng = np.random.default_rng(140)
+    T, Hq, Hkv, d, hi, topk = 60, 2, 1, 8, 5, 2
+    q = rng.standard_normal((T, Hq, d))
+    k = np.repeat(rng.standard_normal((1, Hkv, d)), T, axis=0)
+    v = rng.standard_normal((T, Hkv, d))
+    _, starts, kept = O.decode_sequence(q, k, v, 2, hi, 0.5, topk, 0.3)
+    assert starts == list(range(0, T, hi))
+    for t in range(T):
+        closed = t // hi
+        for h in range(Hq):
+            assert kept[t][h] == list(range(min(topk, closed))), (t, h, kept[t][h])
+
+
 ALL_PINS = [pin_golden, pin_summary_closed_forms, pin_scores_bruteforce, pin_topk_bruteforce,
             pin_kept_invariants, pin_dense_special_case, pin_token_level_bruteforce, pin_row_sum_and_lse,
             pin_causality, pin_gqa_and_permutation, pin_ragged_equals_separate, pin_grouped_routing,
-            pin_chunking_golden, pin_chunking_closed_forms, pin_chunking_rule_invariants, pin_similarity_library]
+            pin_chunking_golden, pin_chunking_closed_forms, pin_chunking_rule_invariants, pin_similarity_library,
+            pin_decode_cuts_match_offline, pin_decode_chunk_end_equals_prefill,
+            pin_decode_dense_equals_causal_attention, pin_decode_first_output_and_groups,
+            pin_decode_ties_to_lower_index]

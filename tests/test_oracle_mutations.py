@@ -15,6 +15,7 @@ import oracle_pins
 ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
 SRC = os.path.join(ORACLE_DIR, "dhsa_oracle.py")
 CHUNK_SRC = os.path.join(ORACLE_DIR, "chunking_oracle.py")
+DECODE_SRC = os.path.join(ORACLE_DIR, "decode_oracle.py")
 
 MUTATIONS = {
     "plain_mean": ("out[c] = mean * np.sqrt(n)", "out[c] = mean"),
@@ -68,27 +69,44 @@ CHUNK_MUTATIONS = {
 }
 
 
-def _mutant(old, new, chunking=False):
+DECODE_MUTATIONS = {
+    "decode_routes_by_token_query": ("                qv = q_open[h]\n", "                qv = q[t, h]\n"),
+    "decode_skips_current_token": ("[np.arange(c0, t + 1)]", "[np.arange(c0, max(t, c0 + 1))]"),
+    "decode_cut_ignores_lo": ("if t > 0 and ((t - c0 >= lo and sim[t] < tau32) or t - c0 >= hi):",
+                              "if t > 0 and (sim[t] < tau32 or t - c0 >= hi):"),
+    "decode_no_query_reset": ("            q_run[:] = 0.0\n", ""),
+    "decode_summary_mean": ("k_sums.append((k_run / np.sqrt(t - c0)).astype(np.float32))",
+                            "k_sums.append((k_run / (t - c0)).astype(np.float32))"),
+    "decode_budget_plus_one": ("chosen = np.sort(order[:min(topk, C)])", "chosen = np.sort(order[:min(topk + 1, C)])"),
+    "decode_values_head0": ("out_t[h] = (w @ v[keys, g, :]) / w.sum()", "out_t[h] = (w @ v[keys, 0, :]) / w.sum()"),
+    "decode_ties_to_higher": ("order = np.lexsort((np.arange(C), -s.astype(np.float64)))",
+                              "order = np.lexsort((-np.arange(C), -s.astype(np.float64)))"),
+}
+
+
+def _mutant(old, new, target=SRC):
     srcs = {}
-    for path in (SRC, CHUNK_SRC):
+    for path in (SRC, CHUNK_SRC, DECODE_SRC):
         with open(path) as f:
             srcs[path] = f.read()
-    target = CHUNK_SRC if chunking else SRC
     assert srcs[target].count(old) == 1, f"mutation anchor not found exactly once: {old!r}"
     srcs[target] = srcs[target].replace(old, new)
     mod = types.ModuleType("oracle_mutant")
     for path, src in srcs.items():
+        # one namespace holds every file, so the package-relative imports are dropped
+        src = "\n".join(l for l in src.split("\n") if not l.startswith("from ."))
         exec(compile(src, os.path.basename(path), "exec"), mod.__dict__)
     return mod
 
 
-ALL = {**{n: (m, False) for n, m in MUTATIONS.items()}, **{n: (m, True) for n, m in CHUNK_MUTATIONS.items()}}
+ALL = {**{n: (m, SRC) for n, m in MUTATIONS.items()}, **{n: (m, CHUNK_SRC) for n, m in CHUNK_MUTATIONS.items()},
+       **{n: (m, DECODE_SRC) for n, m in DECODE_MUTATIONS.items()}}
 
 
 @pytest.mark.parametrize("name", sorted(ALL))
 def test_mutant_is_caught(name):
-    (old, new), chunking = ALL[name]
-    mod = _mutant(old, new, chunking)
+    (old, new), target = ALL[name]
+    mod = _mutant(old, new, target)
     caught = []
     for pin in oracle_pins.ALL_PINS:
         try:
