@@ -135,6 +135,64 @@ def stage_protocol(torch, stages, reps: int = 20):
     return [(float(np.median(t)), float(np.min(t))) for t in times]
 
 
+def decode_measure(torch, D, w, q, k, v, batch: int, steps: int = 30, warmup: int = 5):
+    """Decode against the kept structure (an extension, not part of the step): ``batch`` copies of the
+    workload's first sequence as the context, chunked by this library's rule, loaded into a decode
+    state; then one-token steps (routing once per KV head, top-k of the workload).  Algorithmic bytes per
+    step: the kept K and V rows of every (sequence, KV head) plus the closed chunks' key summaries."""
+    T = int(w.cu_seqlens[1])
+    Hq, Hkv, d = w.num_q_heads, w.num_kv_heads, w.head_dim
+    topk = int(w.topk.max())
+    lo, hi, tau = 32, 1024, 0.5
+    cc, scs = D.online_chunks(k[:T], w.cu_seqlens[:2], lo, hi, tau)
+    C = len(cc) - 1
+    cu_b = np.arange(batch + 1, dtype=np.int32) * T
+    cc_b = np.concatenate([[0]] + [cc[1:] + b * T for b in range(batch)]).astype(np.int32)
+    scs_b = np.arange(batch + 1, dtype=np.int32) * C
+    lay = D.Layout(cu_b, cc_b, scs_b, Hq, Hkv, d, q.dtype)
+    st = D.DecodeState(batch, Hq, Hkv, d, q.dtype, T + warmup + steps + 1, 1024)
+    st.load_prefix(lay, q[:T].repeat(batch, 1, 1), k[:T].repeat(batch, 1, 1), v[:T].repeat(batch, 1, 1))
+    # new tokens: rows of the sequence's last chunk, so the open chunk keeps growing with its topic
+    src = torch.arange(T - 64, T, device=q.device)
+    kept = torch.empty((batch, Hq, topk), dtype=torch.int32, device=q.device)
+    out = torch.empty((batch, Hq, d), dtype=q.dtype, device=q.device)
+
+    def step(i):
+        r = src[i % 64].repeat(batch)
+        st.step(q[r].contiguous(), k[r].contiguous(), v[r].contiguous(), lo, hi, tau, topk, True, w.softmax_scale,
+                out=out, kept=kept)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    t_step = e0.elapsed_time(e1) / steps * 1e-3
+    # bytes of the last step: kept closed chunks (per KV head: the same list for its query heads)
+    starts = st.chunk_start.cpu().numpy()
+    ncl = st.num_closed.cpu().numpy()
+    seql = st.seq_len.cpu().numpy()
+    kp = kept.cpu().numpy()
+    G = Hq // Hkv
+    kept_tok = 0
+    for b in range(batch):
+        lens = np.diff(starts[b, :ncl[b] + 1])
+        open_len = int(seql[b] - starts[b, ncl[b]])
+        for g in range(Hkv):
+            ids = kp[b, g * G][kp[b, g * G] >= 0]
+            kept_tok += int(lens[ids].sum()) + open_len
+    b_step = kept_tok * d * 2 * 2 + int(ncl.sum()) * Hkv * d * 4 + batch * (Hq + 2 * Hkv) * d * 2 * 2
+    return {"context_tokens": T, "batch": batch, "routing": "per_kv_head", "topk": topk,
+            "chunk_rule": f"cosine < {tau}, lengths [{lo}, {hi}]", "closed_chunks": int(ncl[0]),
+            "ms_per_step": t_step * 1e3, "tokens_per_s": batch / t_step,
+            "kept_tokens_per_kv_head": kept_tok / (batch * Hkv), "bytes_per_step": b_step,
+            "hbm_GBps": b_step / t_step / 1e9, "hbm_frac": b_step / t_step / 1e9 / PEAK_HBM_GBS}
+
+
 def traffic_record(workload: str):
     """HBM traffic of stage 3 from committed rocprofv3 counter runs, if they match the kernel source."""
     path = os.path.join(ROOT, "profiles", f"prefill_bf16_{workload}_traffic.json")
@@ -198,6 +256,8 @@ def main() -> int:
     ap.add_argument("--routing", choices=("head", "kv-group"), default="head",
                     help="route per query head (default) or once per KV head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-batch", type=int, default=8,
+                    help="sequences in the decode measurement at the workload's context (0: skip it)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for the baseline")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -329,6 +389,9 @@ def main() -> int:
         "stages12_hbm_frac_median": (b1 + b2) / (p1 + p2) / 1e9 / PEAK_HBM_GBS,
         "prefill_frac_median": F3 / p3 / 1e12 / peak,
         "protocol": "20 reps, each after an untimed 1 GiB read evicting L2 and the last-level cache with clean lines"}
+    if bf16 and args.decode_batch > 0:
+        print("[bench] decode at the workload's context", file=sys.stderr, flush=True)
+        result["decode"] = decode_measure(torch, D, w, q, k, v, args.decode_batch)
     if bf16:
         peaks = achievable_peaks(torch)
         result["roofline"]["achievable_peak_measured"] = peaks["mfma_loop_TFLOPs"]

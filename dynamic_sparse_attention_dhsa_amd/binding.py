@@ -27,7 +27,8 @@ STATUS_NAMES = {0: "DHSA_OK", 1: "DHSA_ERR_NULL_ARG", 2: "DHSA_ERR_BAD_SHAPE", 3
 # every entry point declared in include/dhsa.h
 EXPORTS = ("dhsa_abi_version", "dhsa_status_str", "dhsa_validate_layout", "dhsa_route_plan",
            "dhsa_chunk_summarize", "dhsa_route", "dhsa_route_grouped", "dhsa_sparse_prefill",
-           "dhsa_adjacent_similarity", "dhsa_chunk_boundaries")
+           "dhsa_adjacent_similarity", "dhsa_chunk_boundaries", "dhsa_decode_workspace_bytes",
+           "dhsa_decode_load_prefix", "dhsa_decode_step")
 
 
 class DhsaError(RuntimeError):
@@ -35,6 +36,15 @@ class DhsaError(RuntimeError):
         super().__init__(f"{where}: {message}")
         self.status = status
         self.name = STATUS_NAMES.get(status, str(status))
+
+
+class DecodeStateStruct(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
+                ("max_chunks", ctypes.c_int32), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+                ("seq_len", ctypes.c_void_p), ("num_closed", ctypes.c_void_p), ("chunk_start", ctypes.c_void_p),
+                ("k_sum", ctypes.c_void_p), ("q_run", ctypes.c_void_p), ("k_run", ctypes.c_void_p),
+                ("status", ctypes.c_void_p)]
 
 
 class LayoutStruct(ctypes.Structure):
@@ -77,6 +87,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dhsa_adjacent_similarity.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, ctypes.c_float, vp, vp, vp]
     lib.dhsa_chunk_boundaries.restype = i32
     lib.dhsa_chunk_boundaries.argtypes = [i32, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp]
+    dsp = ctypes.POINTER(DecodeStateStruct)
+    lib.dhsa_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.dhsa_decode_workspace_bytes.argtypes = [dsp, i32, i32]
+    lib.dhsa_decode_load_prefix.restype = i32
+    lib.dhsa_decode_load_prefix.argtypes = [dsp, lp, vp, vp, vp, vp]
+    lib.dhsa_decode_step.restype = i32
+    lib.dhsa_decode_step.argtypes = [dsp, vp, vp, vp, i32, i32, ctypes.c_float, i32, i32, ctypes.c_float, vp, vp,
+                                     vp, ctypes.c_size_t, vp]
     if lib.dhsa_abi_version() != 1:
         raise RuntimeError("libdhsa.so ABI version mismatch")
     _LIB = lib
@@ -312,3 +330,71 @@ def online_chunks(k: torch.Tensor, cu_seqlens, lo: int, hi: int, tau: float) -> 
     cu_chunks, scs, nch = chunk_boundaries(bits, sl, lo, hi)
     C = int(nch.cpu().item())
     return cu_chunks[:C + 1].cpu().numpy(), scs.cpu().numpy()
+
+
+# ----------------------------------------------------------------------------- decode
+
+class DecodeState:
+    """Decode state of a batch (dhsa_decode_state): caches, chunk tables and running sums, all device
+    tensors owned here; ``load_prefix`` hands a chunked prefill batch over, ``step`` appends one token
+    per sequence and returns its attention output."""
+
+    def __init__(self, num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype,
+                 max_tokens: int, max_chunks: int, device="cuda"):
+        dev = torch.device(device)
+        if dtype == torch.bfloat16:
+            code = DHSA_BF16
+        elif dtype == torch.float32:
+            code = DHSA_F32
+        else:
+            raise DhsaError(5, "DecodeState", f"unsupported dtype {dtype}")
+        B, Hq, Hkv, d, L, C = num_seqs, num_q_heads, num_kv_heads, head_dim, max_tokens, max_chunks
+        self.dtype, self.device = dtype, dev
+        self.num_q_heads, self.num_kv_heads, self.head_dim = Hq, Hkv, d
+        self.k_cache = torch.zeros((B, L, Hkv, d), dtype=dtype, device=dev)
+        self.v_cache = torch.zeros((B, L, Hkv, d), dtype=dtype, device=dev)
+        self.seq_len = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.num_closed = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.chunk_start = torch.zeros((B, C + 1), dtype=torch.int32, device=dev)
+        self.k_sum = torch.zeros((B, C, Hkv, d), dtype=torch.float32, device=dev)
+        self.q_run = torch.zeros((B, Hq, d), dtype=torch.float32, device=dev)
+        self.k_run = torch.zeros((B, Hkv, d), dtype=torch.float32, device=dev)
+        self.status = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.struct = DecodeStateStruct(B, Hq, Hkv, d, code, L, C, *(t.data_ptr() for t in (
+            self.k_cache, self.v_cache, self.seq_len, self.num_closed, self.chunk_start, self.k_sum, self.q_run,
+            self.k_run, self.status)))
+        self._ws = {}
+
+    def workspace(self, topk: int, grouped: bool) -> torch.Tensor:
+        key = (int(topk), bool(grouped))
+        if key not in self._ws:
+            n = load_library().dhsa_decode_workspace_bytes(ctypes.byref(self.struct), int(topk), int(grouped))
+            if n == 0:
+                raise DhsaError(2, "dhsa_decode_workspace_bytes", "state or budget not supported")
+            self._ws[key] = torch.empty(n, dtype=torch.uint8, device=self.device)
+        return self._ws[key]
+
+    def load_prefix(self, layout: "Layout", q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> None:
+        layout._check_tensor(q, layout.num_q_heads, "q")
+        layout._check_tensor(k, layout.num_kv_heads, "k")
+        layout._check_tensor(v, layout.num_kv_heads, "v")
+        _check(load_library().dhsa_decode_load_prefix(ctypes.byref(self.struct), ctypes.byref(layout.struct), _ptr(q),
+                                                      _ptr(k), _ptr(v), _stream()), "dhsa_decode_load_prefix")
+
+    def step(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lo: int, hi: int, tau: float, topk: int,
+             grouped: bool = False, softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+             kept: Optional[torch.Tensor] = None) -> torch.Tensor:
+        B = self.seq_len.numel()
+        for t, name, heads in ((q, "q", self.num_q_heads), (k, "k", self.num_kv_heads), (v, "v", self.num_kv_heads)):
+            if not t.is_cuda or t.dtype != self.dtype or tuple(t.shape) != (B, heads, self.head_dim) \
+                    or not t.is_contiguous():
+                raise DhsaError(2, name, f"expected contiguous {self.dtype} [{B}, {heads}, {self.head_dim}] on the GPU")
+        if softmax_scale is None:
+            softmax_scale = 1.0 / math.sqrt(self.head_dim)
+        if out is None:
+            out = torch.empty_like(q)
+        ws = self.workspace(topk, grouped)
+        _check(load_library().dhsa_decode_step(ctypes.byref(self.struct), _ptr(q), _ptr(k), _ptr(v), int(lo), int(hi),
+                                               float(tau), int(topk), int(grouped), float(softmax_scale), _ptr(out),
+                                               _ptr(kept), _ptr(ws), ws.numel(), _stream()), "dhsa_decode_step")
+        return out

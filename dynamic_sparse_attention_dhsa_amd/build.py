@@ -21,7 +21,7 @@ INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 LIB = os.path.join(PKG, "libdhsa.so")
 CALIB_LIB = os.path.join(PKG, "libdhsa_calib.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["api.cpp", "summarize.hip", "route.hip", "prefill_bf16.hip", "prefill_f32.hip", "chunking.hip"]
+SOURCES = ["api.cpp", "summarize.hip", "route.hip", "prefill_bf16.hip", "prefill_f32.hip", "chunking.hip", "decode.hip"]
 CALIB_SOURCES = ["calib.hip"]
 ARCH = "gfx950"
 

@@ -76,6 +76,55 @@ dhsa_status check_row_ptr(const dhsa_layout* L, const int32_t* h_row_ptr, int64_
 
 dhsa_status launched(hipError_t e) { return e == hipSuccess ? DHSA_OK : DHSA_ERR_LAUNCH; }
 
+// Decode state: shapes, capacities and pointers (host-side view only).
+dhsa_status check_decode_state(const dhsa_decode_state* st, dhsa::DecodeDims* dims, dhsa::DecodePtrs* ptrs) {
+  if (st == nullptr) return DHSA_ERR_NULL_ARG;
+  if (st->num_seqs < 1 || st->num_q_heads < 1 || st->num_kv_heads < 1 || st->max_tokens < 1 ||
+      st->max_chunks < 1)
+    return DHSA_ERR_BAD_SHAPE;
+  if (st->num_q_heads % st->num_kv_heads != 0) return DHSA_ERR_BAD_SHAPE;
+  if (st->dtype == DHSA_BF16) {
+    if (st->head_dim != 64 && st->head_dim != 128 && st->head_dim != 256) return DHSA_ERR_UNSUPPORTED;
+  } else if (st->dtype == DHSA_F32) {
+    if (st->head_dim != 64 && st->head_dim != 128) return DHSA_ERR_UNSUPPORTED;
+  } else {
+    return DHSA_ERR_UNSUPPORTED;
+  }
+  if (st->max_chunks > dhsa::kDecodeMaxChunks) return DHSA_ERR_UNSUPPORTED;
+  if ((st->max_tokens + dhsa::kDecodeSlice - 1) / dhsa::kDecodeSlice > dhsa::kDecodeMaxSlices) return DHSA_ERR_UNSUPPORTED;
+  const int64_t elem = st->dtype == DHSA_BF16 ? 2 : 4;
+  if ((int64_t)st->max_tokens * st->num_kv_heads * st->head_dim * elem > ((int64_t)1 << 40)) return DHSA_ERR_UNSUPPORTED;
+  if (st->k_cache == nullptr || st->v_cache == nullptr || st->seq_len == nullptr || st->num_closed == nullptr ||
+      st->chunk_start == nullptr || st->k_sum == nullptr || st->q_run == nullptr || st->k_run == nullptr ||
+      st->status == nullptr)
+    return DHSA_ERR_NULL_ARG;
+  *dims = dhsa::DecodeDims{st->num_seqs, st->num_q_heads, st->num_kv_heads, st->head_dim, st->dtype,
+                           st->max_tokens, st->max_chunks};
+  *ptrs = dhsa::DecodePtrs{st->k_cache, st->v_cache, st->seq_len, st->num_closed, st->chunk_start,
+                           st->k_sum, st->q_run, st->k_run, st->status};
+  return DHSA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace layout of a decode step: spans, span counts, token counts, split-K partial states.
+size_t decode_workspace(const dhsa::DecodeDims& p, int topk, bool grouped, dhsa::DecodeWork* w, void* base) {
+  const size_t rows = (size_t)p.B * (grouped ? p.Hkv : p.Hq);
+  const int NS = (p.L + dhsa::kDecodeSlice - 1) / dhsa::kDecodeSlice;
+  const size_t o_spans = 0;
+  const size_t o_nspan = align256(o_spans + rows * (topk + 1) * sizeof(int4));
+  const size_t o_ntok = align256(o_nspan + rows * sizeof(int32_t));
+  const size_t o_part = align256(o_ntok + rows * sizeof(int32_t));
+  const size_t total = align256(o_part + (size_t)p.B * p.Hq * NS * (p.d + 2) * sizeof(float));
+  if (w != nullptr) {
+    char* c = (char*)base;
+    *w = dhsa::DecodeWork{(int4*)(c + o_spans), (int32_t*)(c + o_nspan), (int32_t*)(c + o_ntok),
+                          (float*)(c + o_part), NS};
+  }
+  return total;
+}
+
+
 // Token offsets of a batch (host mirror): start at 0, monotone, end at T.
 dhsa_status check_seqlens(int32_t B, int32_t T, const int32_t* cu_seqlens, const int32_t* h_cu_seqlens) {
   if (B < 0 || T < 0) return DHSA_ERR_BAD_SHAPE;
@@ -225,6 +274,50 @@ dhsa_status dhsa_chunk_boundaries(int32_t num_seqs, int32_t total_tokens, const 
   const int32_t lo_c = lo < hi_c ? lo : hi_c;
   return launched(dhsa::launch_chunk_walk(num_seqs, total_tokens, cu_seqlens, cut_bits, lo_c, hi_c, cu_chunks,
                                           seq_chunk_start, num_chunks, (hipStream_t)stream));
+}
+
+
+size_t dhsa_decode_workspace_bytes(const dhsa_decode_state* state, int32_t topk, int32_t grouped) {
+  dhsa::DecodeDims p;
+  dhsa::DecodePtrs s;
+  if (check_decode_state(state, &p, &s) != DHSA_OK || topk < 0 || topk >= dhsa::kDecodeMaxChunks) return 0;
+  return decode_workspace(p, topk, grouped != 0, nullptr, nullptr);
+}
+
+dhsa_status dhsa_decode_load_prefix(const dhsa_decode_state* state, const dhsa_layout* prefix, const void* q,
+                                    const void* k, const void* v, void* stream) {
+  dhsa::DecodeDims p;
+  dhsa::DecodePtrs s;
+  dhsa_status st = check_decode_state(state, &p, &s);
+  if (st != DHSA_OK) return st;
+  Plan pl;
+  if ((st = check_layout(prefix, &pl)) != DHSA_OK) return st;
+  if (pl.B != p.B || pl.Hq != p.Hq || pl.Hkv != p.Hkv || pl.d != p.d || pl.dtype != p.dtype) return DHSA_ERR_BAD_SHAPE;
+  for (int32_t b = 0; b < pl.B; ++b) {
+    if (prefix->h_cu_seqlens[b + 1] - prefix->h_cu_seqlens[b] > p.L) return DHSA_ERR_BAD_SHAPE;
+    if (prefix->h_seq_chunk_start[b + 1] - prefix->h_seq_chunk_start[b] > p.Cmax + 1) return DHSA_ERR_BAD_SHAPE;
+  }
+  if (pl.T > 0 && (q == nullptr || k == nullptr || v == nullptr)) return DHSA_ERR_NULL_ARG;
+  return launched(dhsa::launch_decode_load(p, s, pl, q, k, v, (hipStream_t)stream));
+}
+
+dhsa_status dhsa_decode_step(const dhsa_decode_state* state, const void* q, const void* k, const void* v,
+                             int32_t lo, int32_t hi, float tau, int32_t topk, int32_t grouped,
+                             float softmax_scale, void* out, int32_t* kept, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  dhsa::DecodeDims p;
+  dhsa::DecodePtrs s;
+  dhsa_status st = check_decode_state(state, &p, &s);
+  if (st != DHSA_OK) return st;
+  if (lo < 1 || hi < lo || !isfinite(tau)) return DHSA_ERR_BAD_SHAPE;
+  if (topk < 0 || topk >= dhsa::kDecodeMaxChunks) return DHSA_ERR_BAD_BUDGET;
+  if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return DHSA_ERR_BAD_SHAPE;
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || workspace == nullptr) return DHSA_ERR_NULL_ARG;
+  if (((uintptr_t)workspace & 255) != 0) return DHSA_ERR_BAD_SHAPE;
+  dhsa::DecodeWork w;
+  if (decode_workspace(p, topk, grouped != 0, &w, workspace) > workspace_bytes) return DHSA_ERR_BAD_SHAPE;
+  return launched(dhsa::launch_decode_step(p, s, q, k, v, lo, hi, tau, topk, grouped != 0, softmax_scale, out, kept,
+                                           w, (hipStream_t)stream));
 }
 
 }  // extern "C"

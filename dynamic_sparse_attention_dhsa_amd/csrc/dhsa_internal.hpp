@@ -47,6 +47,37 @@ hipError_t launch_adjacent_similarity(int B, int ntok, int W, int dtype, const i
 hipError_t launch_chunk_walk(int B, int ntok, const int32_t* cu_seqlens, const uint64_t* cut_bits, int lo, int hi,
                              int32_t* cu_chunks, int32_t* seq_chunk_start, int32_t* num_chunks, hipStream_t stream);
 
+// Decode (one new token per sequence against the kept structure).
+constexpr int kDecodeSlice = 256;                 // kept tokens per split-K attention workgroup
+constexpr int kDecodeMaxChunks = 1024;            // closed chunks per sequence the routing holds in registers
+constexpr int kDecodeMaxSlices = 4096;            // split-K slices per (sequence, q head): L <= 1M tokens
+struct DecodeDims {
+  int32_t B, Hq, Hkv, d, dtype, L, Cmax;
+};
+struct DecodePtrs {                               // the caller's state (device)
+  void* k_cache;
+  void* v_cache;
+  int32_t* seq_len;
+  int32_t* num_closed;
+  int32_t* chunk_start;
+  float* k_sum;
+  float* q_run;
+  float* k_run;
+  int32_t* status;
+};
+struct DecodeWork {                               // carved from the caller's workspace
+  int4* spans;                                    // [B * rows, topk + 1]
+  int32_t* nspan;                                 // [B * rows]
+  int32_t* ntok;                                  // [B * rows]
+  float* part;                                    // [B * Hq * NS, d + 2]
+  int NS;                                         // slices per (sequence, q head)
+};
+hipError_t launch_decode_step(const DecodeDims& p, const DecodePtrs& s, const void* q, const void* k, const void* v,
+                              int lo, int hi, float tau, int topk, bool grouped, float scale, void* out,
+                              int32_t* kept, const DecodeWork& w, hipStream_t stream);
+hipError_t launch_decode_load(const DecodeDims& p, const DecodePtrs& s, const Plan& pl, const void* q, const void* k,
+                              const void* v, hipStream_t stream);
+
 // Device helpers ----------------------------------------------------------------------------
 
 // Index of the sequence containing chunk c: the last b with seq_chunk_start[b] <= c.

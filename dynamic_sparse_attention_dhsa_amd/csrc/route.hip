@@ -35,72 +35,24 @@
 // Rows with more candidates than the registers hold go to a general kernel
 // that bitonic-sorts all of the row's keys in LDS.
 #include "dhsa_internal.hpp"
+#include "select.hpp"
 
 namespace dhsa {
 namespace {
 
 constexpr int kWaves = 4;
 constexpr int kRegCand = kRouteRegCand;          // candidates held in registers
-constexpr int kRegBatches = kRegCand / 64;       // 64 per batch, one per lane
+constexpr int kRegBatches = sel::kSelBatches;    // 64 per batch, one per lane
+static_assert(kRegCand == sel::kSelCand, "selection capacity");
+using sel::ordered_bits;
 constexpr int kWideThreads = 256;
 constexpr int kMaxCand = 8192;
-
-__device__ inline uint32_t ordered_bits(float s) {
-  uint32_t u = (s == 0.0f) ? 0u : __float_as_uint(s);   // -0 and +0 rank equal
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 __device__ inline uint64_t rank_key(float s, int j) {
   return ((uint64_t)ordered_bits(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
 }
 
 __device__ inline int key_chunk(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
-
-// Selection over the scores held in registers (ob[b]: ordered bits of candidate first + 64 b +
-// lane, 0 where there is no candidate; a finite score never maps to 0 and every trial value is at
-// least 1, so empty slots never count).  NB is the number of batches in use, fixed at compile time
-// so the per-bit count is straight-line code.  Writes the row's kk kept chunks, ascending.
-template <int NB>
-__device__ inline void select_and_write(const uint32_t (&ob)[kRegBatches], int kk, int first, int lane,
-                                        int32_t* __restrict__ out) {
-  // thr: the largest value with at least kk candidates at or above it, i.e. the kk-th best score
-  uint32_t thr = 0u;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t t = thr | (1u << bit);
-    int cnt = 0;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) cnt += __popcll(__ballot(ob[b] >= t));
-    if (cnt >= kk) thr = t;
-  }
-  // Write in chunk order those above thr, then the first ones equal to it until kk are written.
-  int above = 0;
-#pragma unroll
-  for (int b = 0; b < NB; ++b) above += __popcll(__ballot(ob[b] > thr));
-  const int need = kk - above;
-  const uint64_t below = (1ull << lane) - 1ull;
-  int pos = 0, eq_seen = 0;
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const bool eq = ob[b] == thr;              // thr >= 1, so only real candidates
-    const uint64_t eqm = __ballot(eq);
-    const bool keep = ob[b] > thr || (eq && eq_seen + __popcll(eqm & below) < need);
-    eq_seen += __popcll(eqm);
-    const uint64_t km = __ballot(keep);
-    if (keep) out[pos + __popcll(km & below)] = first + 64 * b + lane;
-    pos += __popcll(km);
-  }
-}
-
-template <int NB>
-__device__ inline void select_dispatch(int nb, const uint32_t (&ob)[kRegBatches], int kk, int first, int lane,
-                                       int32_t* __restrict__ out) {
-  if constexpr (NB > kRegBatches) {
-    return;
-  } else {
-    if (nb == NB) select_and_write<NB>(ob, kk, first, lane, out);
-    else select_dispatch<NB + 1>(nb, ob, kk, first, lane, out);
-  }
-}
 
 template <int D, bool GROUPED>
 __global__ __launch_bounds__(kWaves * 64) void route_kernel(
@@ -215,7 +167,7 @@ __global__ __launch_bounds__(kWaves * 64) void route_kernel(
 #pragma unroll
   for (int b = 0; b < kRegBatches; ++b)
     ob[b] = (b < nb && 64 * b + lane < nc) ? ordered_bits(row[64 * b + lane]) : 0u;
-  select_dispatch<1>(nb, ob, kk, first, lane, out);
+  sel::select_dispatch<1>(nb, ob, kk, first, lane, out);
   if (lane == 0) out[kk] = i;
 }
 

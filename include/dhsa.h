@@ -201,6 +201,72 @@ dhsa_status dhsa_chunk_boundaries(int32_t num_seqs, int32_t total_tokens, const 
                                   int32_t* cu_chunks, int32_t* seq_chunk_start, int32_t* num_chunks,
                                   void* stream);
 
+/* ---- Decode: one new token per sequence, against the kept structure (an
+ * extension; the pages evaluate prefill only - "Long-Context Modeling with
+ * Dynamic Hierarchical Sparse Attention for On-Device LLMs", Abstract; ICML 2026
+ * page, Abstract - and describe the method as online).  This library's reading:
+ * the new token joins the open (last) chunk unless the chunking rule above cuts
+ * before it ((t - c0 >= lo and cos(K[t-1], K[t]) < tau) or t - c0 >= hi); a
+ * chunk's key summary (sum of its key rows / sqrt(size)) is kept when it closes;
+ * the open chunk's query summary so far, (sum of q over c0..t) / sqrt(t - c0 + 1),
+ * scores the closed chunks; the top-k by (score desc, chunk asc) plus the open
+ * chunk are kept; the token attends exactly to their tokens up to itself.  At a
+ * chunk's last token this equals prefill at that token.
+ *
+ * The state is the caller's (device memory, sizes as shown; B sequences,
+ * capacity L tokens and C closed chunks each). */
+typedef struct dhsa_decode_state {
+  int32_t num_seqs;          /* B >= 1                                            */
+  int32_t num_q_heads;       /* Hq                                                */
+  int32_t num_kv_heads;      /* Hkv, Hq % Hkv == 0                                */
+  int32_t head_dim;          /* d: 64, 128, 256 (bf16) or 64, 128 (fp32)          */
+  int32_t dtype;             /* dhsa_dtype of the cache, q, k, v, out             */
+  int32_t max_tokens;        /* 1 <= L <= 2^20: cache capacity per sequence       */
+  int32_t max_chunks;        /* C, 1 <= C <= 1024: closed chunks per sequence     */
+  void* k_cache;             /* [B, L, Hkv, d]                                    */
+  void* v_cache;             /* [B, L, Hkv, d]                                    */
+  int32_t* seq_len;          /* [B] tokens in the cache                           */
+  int32_t* num_closed;       /* [B] closed chunks                                 */
+  int32_t* chunk_start;      /* [B, C + 1] chunk starts (token offsets in the
+                                sequence); entry num_closed is the open chunk's   */
+  float* k_sum;              /* [B, C, Hkv, d] key summaries of closed chunks     */
+  float* q_run;              /* [B, Hq, d] sum of q over the open chunk           */
+  float* k_run;              /* [B, Hkv, d] sum of k over the open chunk          */
+  int32_t* status;           /* [B] 0; 1 once the cache was full, 2 once the chunk
+                                table was full: that sequence then stays as it was
+                                and its outputs are zeros                          */
+} dhsa_decode_state;
+
+/* Workspace bytes dhsa_decode_step needs for this state and budget (host only). */
+size_t dhsa_decode_workspace_bytes(const dhsa_decode_state* state, int32_t topk, int32_t grouped);
+
+/* Load the prefix of each sequence from a chunked batch (the layout of the
+ * prefill calls; B equal to the state's): key/value rows into the cache, key
+ * summaries of every chunk but each sequence's last, which becomes the open
+ * chunk (its q and k sums are kept), counters set, status cleared.  q [T, Hq, d],
+ * k, v [T, Hkv, d] as in prefill.  The chunks should come from the same rule
+ * (dhsa_chunk_boundaries with the lo, hi, tau later given to dhsa_decode_step)
+ * for decode to continue it.  Errors: shapes or dtypes differing from the
+ * state's, a sequence longer than L or with more than C + 1 chunks. */
+dhsa_status dhsa_decode_load_prefix(const dhsa_decode_state* state, const dhsa_layout* prefix, const void* q,
+                                    const void* k, const void* v, void* stream);
+
+/* One decode step for every sequence: append token (q [B, Hq, d], k, v [B, Hkv, d]),
+ * then write out [B, Hq, d] (its attention output, dtype of the state).
+ *   lo, hi, tau     the chunking rule (1 <= lo <= hi, tau finite)
+ *   topk            closed chunks kept per row, 0 <= topk <= 1023
+ *   grouped         0: routing per query head; 1: once per KV head (group-summed
+ *                   query summaries, the same kept chunks for the group)
+ *   softmax_scale   > 0
+ *   kept            optional device int32 [B, Hq, topk]: the kept closed chunks,
+ *                   ascending, -1 padded (NULL: not written)
+ *   workspace       device, >= dhsa_decode_workspace_bytes(state, topk, grouped),
+ *                   256-byte aligned; contents are scratch between calls */
+dhsa_status dhsa_decode_step(const dhsa_decode_state* state, const void* q, const void* k, const void* v,
+                             int32_t lo, int32_t hi, float tau, int32_t topk, int32_t grouped,
+                             float softmax_scale, void* out, int32_t* kept, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -214,3 +214,44 @@ def test_chunking_calls_reject_before_launch():
     assert walk(h_cs=None) == NULL
     assert walk(bits=0) == NULL
     assert walk(out=0) == NULL
+
+
+def test_decode_calls_reject_before_launch():
+    lib = Bd.load_library()
+    vp = ctypes.c_void_p
+
+    def state(**kw):
+        f = dict(num_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=128, dtype=1, max_tokens=4096, max_chunks=256)
+        f.update(kw)
+        ptrs = [FAKE] * 9
+        return Bd.DecodeStateStruct(f["num_seqs"], f["num_q_heads"], f["num_kv_heads"], f["head_dim"], f["dtype"],
+                                    f["max_tokens"], f["max_chunks"], *ptrs)
+
+    def step(st, lo=8, hi=64, tau=0.5, topk=4, scale=0.1, ws=FAKE * 256, nbytes=1 << 30, out=FAKE):
+        return lib.dhsa_decode_step(ctypes.byref(st), vp(FAKE), vp(FAKE), vp(FAKE), lo, hi, tau, topk, 0, scale,
+                                    vp(out) if out else None, None, vp(ws), nbytes, None)
+
+    good = state()
+    assert lib.dhsa_decode_workspace_bytes(ctypes.byref(good), 4, 0) > 0
+    assert lib.dhsa_decode_workspace_bytes(ctypes.byref(state(max_chunks=2000)), 4, 0) == 0
+    assert step(state(num_q_heads=6, num_kv_heads=4)) == SHAPE
+    assert step(state(head_dim=96)) == UNSUP
+    assert step(state(dtype=0, head_dim=256)) == UNSUP
+    assert step(state(max_chunks=1025)) == UNSUP
+    assert step(good, lo=0) == SHAPE
+    assert step(good, hi=4) == SHAPE
+    assert step(good, tau=float("inf")) == SHAPE
+    assert step(good, topk=-1) == BUDGET
+    assert step(good, topk=1024) == BUDGET
+    assert step(good, scale=0.0) == SHAPE
+    assert step(good, out=0) == NULL
+    assert step(good, ws=FAKE + 8) == SHAPE                   # misaligned workspace
+    assert step(good, nbytes=64) == SHAPE                     # too small
+    bad = state()
+    bad.q_run = None
+    assert step(bad) == NULL
+    # a prefix whose shapes differ from the state's, or a sequence longer than the cache
+    m = Mirror([0, 10, 17], [0, 4, 10, 13, 17], [0, 2, 4], Hq=8, Hkv=2, d=128)
+    assert lib.dhsa_decode_load_prefix(ctypes.byref(state(num_seqs=3)), m.ref(), vp(FAKE), vp(FAKE), vp(FAKE), None) == SHAPE
+    assert lib.dhsa_decode_load_prefix(ctypes.byref(state(max_tokens=8)), m.ref(), vp(FAKE), vp(FAKE), vp(FAKE), None) == SHAPE
+    assert lib.dhsa_decode_load_prefix(ctypes.byref(state(max_chunks=0)), m.ref(), vp(FAKE), vp(FAKE), vp(FAKE), None) == SHAPE
