@@ -231,7 +231,8 @@ def kept_token_mask(row_ptr, block_idx_h, cu_chunks) -> np.ndarray:
     T = int(cc[-1])
     keep_chunk = np.zeros((C, C), bool)
     for i in range(C):
-        keep_chunk[i, block_idx_h[row_ptr[i]:row_ptr[i + 1]]] = True
+        row = np.asarray(block_idx_h[row_ptr[i]:row_ptr[i + 1]])
+        keep_chunk[i, row[row >= 0]] = True     # -1 entries pad rows of variable length
     tok_chunk = np.repeat(np.arange(C), np.diff(cc))
     mask = keep_chunk[np.ix_(tok_chunk, tok_chunk)]
     return mask & (np.arange(T)[None, :] <= np.arange(T)[:, None])
@@ -266,6 +267,7 @@ def attend(q, k, v, cu_chunks, row_ptr, block_idx, softmax_scale: float,
         for i in chunks:
             s_i, e_i = cc[i], cc[i + 1]
             kept = block_idx[h, row_ptr[i]:row_ptr[i + 1]]
+            kept = kept[kept >= 0]              # -1 entries pad rows of variable length
             keys = np.concatenate([np.arange(cc[j], cc[j + 1]) for j in kept])
             qi = q[s_i:e_i, h, :].astype(np.float64)
             Z = softmax_scale * (qi @ k[keys, g, :].astype(np.float64).T)

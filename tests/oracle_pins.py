@@ -539,10 +539,93 @@ def pin_decode_ties_to_lower_index(O):
             assert kept[t][h] == list(range(min(topk, closed))), (t, h, kept[t][h])
 
 
+# ----------------------------------------------------------------------------- token budget
+
+def _budget_workload(seed, lens_per_seq, Hq=4, Hkv=2, d=8):
+    cs, cc, scs = _layout_from_lengths(lens_per_seq)
+    rng = np.random.default_rng(seed)
+    T = int(cs[-1])
+    q = rng.standard_normal((T, Hq, d))
+    k = rng.standard_normal((T, Hkv, d))
+    v = rng.standard_normal((T, Hkv, d))
+    return cs, cc, scs, q, k, v
+
+
+def pin_budget_equal_lengths_is_topk(O):
+    """All chunks of length L: a budget of b tokens keeps exactly the top floor(b / L) chunks."""
+    L = 3
+    cs, cc, scs, q, k, v = _budget_workload(150, [[L] * 9, [L] * 6])
+    qs, ks = O.chunk_summaries(q, cc), O.chunk_summaries(k, cc)
+    rng = np.random.default_rng(151)
+    budget = rng.integers(0, 8 * L, size=int(scs[-1])).astype(np.int32)
+    for grouped in (False, True):
+        rp_t, bi_t, _ = O.route_tokens(qs, ks, cc, scs, budget, grouped=grouped)
+        rp_k, bi_k, _ = (O.route_grouped if grouped else O.route)(qs, ks, scs, budget // L)
+        assert np.array_equal(rp_t, rp_k) and np.array_equal(bi_t, bi_k)
+
+
+def pin_budget_prefix_bruteforce(O):
+    """Each row is the longest prefix of the (score desc, chunk asc) ranking that fits, checked with
+    Python's sorted() on the chunk scores; -1 pads the row after the diagonal; the capacity equals the
+    count of the shortest earlier chunks that fit."""
+    rng = np.random.default_rng(152)
+    for trial in range(12):
+        lens = [rng.integers(1, 9, size=rng.integers(1, 9)).tolist() for _ in range(rng.integers(1, 3))]
+        cs, cc, scs, q, k, v = _budget_workload(153 + trial, lens)
+        C = int(scs[-1])
+        budget = rng.integers(0, 25, size=C).astype(np.int32)
+        qs, ks = O.chunk_summaries(q, cc), O.chunk_summaries(k, cc)
+        rp, bi, S = O.route_tokens(qs, ks, cc, scs, budget)
+        L = np.diff(cc)
+        for i in range(C):
+            b = max(x for x in range(len(scs) - 1) if scs[x] <= i)
+            first = int(scs[b])
+            cap, tot = 0, 0
+            for n in sorted(L[first:i]):
+                if tot + n > budget[i]:
+                    break
+                tot += n
+                cap += 1
+            assert rp[i + 1] - rp[i] == cap + 1
+            for h in range(q.shape[1]):
+                rank = sorted(range(first, i), key=lambda j: (-float(S[h, i, j]), j))
+                want, tot = [], 0
+                for j in rank:
+                    if tot + L[j] > budget[i]:
+                        break
+                    tot += L[j]
+                    want.append(j)
+                row = bi[h, rp[i]:rp[i + 1]].tolist()
+                m = len(want)
+                assert row[:m + 1] == sorted(want) + [i] and all(x == -1 for x in row[m + 1:]), (i, h, row, want)
+
+
+def pin_budget_extremes_and_padding(O):
+    cs, cc, scs, q, k, v = _budget_workload(160, [[2, 5, 3, 4, 1, 6]])
+    qs, ks = O.chunk_summaries(q, cc), O.chunk_summaries(k, cc)
+    C = int(scs[-1])
+    rp, bi, _ = O.route_tokens(qs, ks, cc, scs, np.zeros(C, np.int32))
+    assert np.array_equal(rp, np.arange(C + 1)) and np.array_equal(bi[0], np.arange(C))
+    rp, bi, _ = O.route_tokens(qs, ks, cc, scs, np.full(C, 10 ** 6, np.int32))
+    for i in range(C):
+        assert bi[0, rp[i]:rp[i + 1]].tolist() == list(range(i + 1))
+    # attention ignores the padding: a padded list gives the same output as the same list compacted
+    budget = np.array([0, 3, 4, 6, 2, 9], np.int32)
+    rp, bi, _ = O.route_tokens(qs, ks, cc, scs, budget)
+    rows = [[[x for x in bi[h, rp[i]:rp[i + 1]] if x >= 0] for i in range(C)] for h in range(q.shape[1])]
+    a, la = O.attend(q, k, v, cc, rp, bi, 0.3)
+    for h in range(q.shape[1]):
+        rp_c = np.concatenate([[0], np.cumsum([len(r) for r in rows[h]])]).astype(np.int32)
+        bi_c = np.concatenate(rows[h]).astype(np.int32)[None, :].repeat(q.shape[1], axis=0)
+        b_, lb = O.attend(q, k, v, cc, rp_c, bi_c, 0.3, heads=[h])
+        assert np.allclose(a[:, h], b_[:, h], atol=1e-12) and np.allclose(la[h], lb[h], atol=1e-12)
+
+
 ALL_PINS = [pin_golden, pin_summary_closed_forms, pin_scores_bruteforce, pin_topk_bruteforce,
             pin_kept_invariants, pin_dense_special_case, pin_token_level_bruteforce, pin_row_sum_and_lse,
             pin_causality, pin_gqa_and_permutation, pin_ragged_equals_separate, pin_grouped_routing,
             pin_chunking_golden, pin_chunking_closed_forms, pin_chunking_rule_invariants, pin_similarity_library,
             pin_decode_cuts_match_offline, pin_decode_chunk_end_equals_prefill,
             pin_decode_dense_equals_causal_attention, pin_decode_first_output_and_groups,
-            pin_decode_ties_to_lower_index]
+            pin_decode_ties_to_lower_index, pin_budget_equal_lengths_is_topk, pin_budget_prefix_bruteforce,
+            pin_budget_extremes_and_padding]

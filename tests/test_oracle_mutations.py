@@ -16,6 +16,7 @@ ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file
 SRC = os.path.join(ORACLE_DIR, "dhsa_oracle.py")
 CHUNK_SRC = os.path.join(ORACLE_DIR, "chunking_oracle.py")
 DECODE_SRC = os.path.join(ORACLE_DIR, "decode_oracle.py")
+BUDGET_SRC = os.path.join(ORACLE_DIR, "budget_oracle.py")
 
 MUTATIONS = {
     "plain_mean": ("out[c] = mean * np.sqrt(n)", "out[c] = mean"),
@@ -84,9 +85,21 @@ DECODE_MUTATIONS = {
 }
 
 
+BUDGET_MUTATIONS = {
+    "budget_strict_fit": ('m = int(np.searchsorted(cum, budget, side="right"))',
+                          'm = int(np.searchsorted(cum, budget, side="left"))'),
+    "budget_skips_misfits": ('m = int(np.searchsorted(cum, budget, side="right"))',
+                             'm = int(np.sum(np.asarray(lens, np.int64)[cand[order]] <= budget))'),
+    "budget_rank_ascending": ("order = np.lexsort((cand, -s))              # ranking: score desc, then chunk asc",
+                              "order = np.lexsort((cand, s))              # ranking: score desc, then chunk asc"),
+    "budget_plan_longest_first": ("earlier = np.sort(lens[sc[seq[i]]:i])", "earlier = np.sort(lens[sc[seq[i]]:i])[::-1]"),
+    "budget_pad_with_diagonal": ("block_idx = np.full((Hq, nnz), -1, np.int32)", "block_idx = np.full((Hq, nnz), 0, np.int32)"),
+}
+
+
 def _mutant(old, new, target=SRC):
     srcs = {}
-    for path in (SRC, CHUNK_SRC, DECODE_SRC):
+    for path in (SRC, CHUNK_SRC, DECODE_SRC, BUDGET_SRC):
         with open(path) as f:
             srcs[path] = f.read()
     assert srcs[target].count(old) == 1, f"mutation anchor not found exactly once: {old!r}"
@@ -100,7 +113,8 @@ def _mutant(old, new, target=SRC):
 
 
 ALL = {**{n: (m, SRC) for n, m in MUTATIONS.items()}, **{n: (m, CHUNK_SRC) for n, m in CHUNK_MUTATIONS.items()},
-       **{n: (m, DECODE_SRC) for n, m in DECODE_MUTATIONS.items()}}
+       **{n: (m, DECODE_SRC) for n, m in DECODE_MUTATIONS.items()},
+       **{n: (m, BUDGET_SRC) for n, m in BUDGET_MUTATIONS.items()}}
 
 
 @pytest.mark.parametrize("name", sorted(ALL))
