@@ -40,7 +40,8 @@ PREFILL_SRC = os.path.join(ROOT, "dynamic_sparse_attention_dhsa_amd", "csrc", "p
 
 
 def kept_flops(block_idx: np.ndarray, row_ptr: np.ndarray, cu_chunks: np.ndarray, d: int) -> float:
-    """Algorithmic FLOPs of stage 3: 4*d per kept (query, key) pair (QK^T and PV, 2 FLOPs per MAC)."""
+    """Algorithmic FLOPs of stage 3: 4*d per kept (query, key) pair (QK^T and PV, 2 FLOPs per MAC).
+    Entries of -1 (the padding of token-budget rows) keep nothing."""
     lens = np.diff(cu_chunks).astype(np.int64)
     C = lens.size
     total = 0
@@ -48,7 +49,8 @@ def kept_flops(block_idx: np.ndarray, row_ptr: np.ndarray, cu_chunks: np.ndarray
     for h in range(block_idx.shape[0]):
         kept = block_idx[h].astype(np.int64)
         diag = kept == row_of
-        off = np.bincount(row_of[~diag], weights=lens[kept[~diag]], minlength=C)
+        offd = ~diag & (kept >= 0)
+        off = np.bincount(row_of[offd], weights=lens[kept[offd]], minlength=C)
         total += float((lens * off).sum() + (lens * (lens + 1) // 2).sum())
     return 4.0 * d * total
 
@@ -59,6 +61,37 @@ def stage_bytes(T, C, Hq, Hkv, d, s, nnz):
     b1 = T * (Hq + Hkv) * d * s + C * (Hq + Hkv) * d * 4
     b2 = C * (Hq + Hkv) * d * 4 + (C + 1) * 4 + C * 4 + Hq * nnz * 4
     return b1, b2
+
+
+def memory_report(torch, D, w, q, k, v, grouped: bool, token_budget=None):
+    """Device memory of one whole-path call (dhsa.prefill: plan upload, summaries, block list, output)
+    measured with torch's allocator statistics (the library allocates nothing itself), beside the
+    inputs and what dense attention over the same causal pairs would hold."""
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    if token_budget is None:
+        r = D.prefill(q, k, v, w.cu_seqlens, w.cu_chunks, w.seq_chunk_start, w.topk, w.softmax_scale,
+                      grouped=grouped)
+    else:
+        r = D.prefill(q, k, v, w.cu_seqlens, w.cu_chunks, w.seq_chunk_start, token_budget=token_budget,
+                      softmax_scale=w.softmax_scale, grouped=grouped)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    out_b = r["out"].numel() * r["out"].element_size()
+    parts = {"q_sum_k_sum": (r["q_sum"].numel() + r["k_sum"].numel()) * 4,
+             "block_idx": r["block_idx"].numel() * 4}
+    T, Hq = w.total_tokens, w.num_q_heads
+    s = q.element_size()
+    pairs = sum(int(n) * int(n) for n in np.diff(w.cu_seqlens))
+    del r
+    return {"peak_bytes_above_inputs_measured": int(peak), "output_bytes": int(out_b),
+            "path_extra_bytes_measured": int(peak - out_b), "path_extra_parts": parts,
+            "inputs_qkv_bytes": int(q.numel() * s + k.numel() * s + v.numel() * s),
+            "dense_eager_score_bytes": int(Hq * pairs * s),
+            "dense_fused_extra_bytes": int(Hq * T * 4),
+            "note": "dense_eager = the [Hq, L, L] score matrix of unfused attention in the input dtype "
+                    "(computed, not allocated); dense_fused = a fused kernel's fp32 row statistics"}
 
 
 def achievable_peaks(torch):
@@ -384,6 +417,22 @@ def main() -> int:
         "similarity_median_min_ms": [p_s * 1e3, m_s * 1e3], "walk_median_min_ms": [p_w * 1e3, m_w * 1e3],
         "similarity_bytes": b_sim, "similarity_GBps": b_sim / p_s / 1e9,
         "similarity_hbm_frac": b_sim / p_s / 1e9 / PEAK_HBM_GBS}
+    # routing under a token budget: every row gets the mean kept tokens of the chunk budget
+    # (top-k x mean chunk length), then the prefill on its padded lists
+    tok = int(round(float(w.topk.mean()) * T / max(C, 1)))
+    tplan = D.TokenPlan(layout, np.full(C, tok, np.int32))
+    tb_idx = torch.empty((Hq, tplan.nnz), dtype=torch.int32, device="cuda")
+    print("[bench] token-budget routing", file=sys.stderr, flush=True)
+    (p_t, m_t), (p_tp, m_tp) = stage_protocol(torch, [
+        lambda: D.route_tokens(layout, tplan, q_sum, k_sum, tb_idx, grouped=grouped),
+        lambda: D.sparse_prefill(layout, tplan, q, k, v, tb_idx, w.softmax_scale, out=out)])
+    F3t = kept_flops(tb_idx.cpu().numpy(), tplan.h_row_ptr, w.cu_chunks, d)
+    result["stages"]["token_budget"] = {
+        "tokens_per_row": tok, "row_capacity_entries": tplan.nnz, "route_median_min_ms": [p_t * 1e3, m_t * 1e3],
+        "prefill_median_min_ms": [p_tp * 1e3, m_tp * 1e3], "prefill_TFLOPs": F3t / p_tp / 1e12,
+        "kept_density_vs_causal": F3t / (4.0 * d * causal_pairs)}
+    print("[bench] memory report", file=sys.stderr, flush=True)
+    result["memory"] = memory_report(torch, D, w, q, k, v, grouped)
     result["stages"]["cold_cache_median_min_ms"] = {
         "summarize": [p1 * 1e3, m1 * 1e3], "route": [p2 * 1e3, m2 * 1e3], "prefill": [p3 * 1e3, m3 * 1e3],
         "stages12_hbm_frac_median": (b1 + b2) / (p1 + p2) / 1e9 / PEAK_HBM_GBS,

@@ -5,4 +5,5 @@ functions re-exported here (from ``binding``) only marshal torch tensors into
 the C ABI declared in ``include/dhsa.h``.
 """
 from .binding import (DecodeState, DhsaError, Layout, RoutePlan, adjacent_similarity, chunk_boundaries,  # noqa: F401
-                      SeqLayout, chunk_summarize, load_library, online_chunks, prefill, route, sparse_prefill)
+                      SeqLayout, TokenPlan, chunk_summarize, load_library, online_chunks, prefill, route,
+                      route_tokens, sparse_prefill)

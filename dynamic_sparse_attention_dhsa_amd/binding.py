@@ -28,7 +28,7 @@ STATUS_NAMES = {0: "DHSA_OK", 1: "DHSA_ERR_NULL_ARG", 2: "DHSA_ERR_BAD_SHAPE", 3
 EXPORTS = ("dhsa_abi_version", "dhsa_status_str", "dhsa_validate_layout", "dhsa_route_plan",
            "dhsa_chunk_summarize", "dhsa_route", "dhsa_route_grouped", "dhsa_sparse_prefill",
            "dhsa_adjacent_similarity", "dhsa_chunk_boundaries", "dhsa_decode_workspace_bytes",
-           "dhsa_decode_load_prefix", "dhsa_decode_step")
+           "dhsa_decode_load_prefix", "dhsa_decode_step", "dhsa_route_plan_tokens", "dhsa_route_tokens")
 
 
 class DhsaError(RuntimeError):
@@ -76,6 +76,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dhsa_validate_layout.argtypes = [lp]
     lib.dhsa_route_plan.restype = i32
     lib.dhsa_route_plan.argtypes = [lp, vp, vp, ctypes.POINTER(i64)]
+    lib.dhsa_route_plan_tokens.restype = i32
+    lib.dhsa_route_plan_tokens.argtypes = [lp, vp, vp, ctypes.POINTER(i64)]
+    lib.dhsa_route_tokens.restype = i32
+    lib.dhsa_route_tokens.argtypes = [lp, vp, vp, vp, vp, vp, vp, i64, i32, vp, vp]
     lib.dhsa_chunk_summarize.restype = i32
     lib.dhsa_chunk_summarize.argtypes = [lp, vp, vp, vp, vp, vp]
     for name in ("dhsa_route", "dhsa_route_grouped"):
@@ -186,6 +190,25 @@ class RoutePlan:
         return self
 
 
+class TokenPlan(RoutePlan):
+    """CSR row pointers for a per-chunk token budget (dhsa_route_plan_tokens): row i holds the most
+    chunks any ranking could keep, so rows carry -1 padding after their diagonal."""
+
+    def __init__(self, layout: Layout, token_budget):
+        lib = load_library()
+        self.h_topk = None
+        self.h_token_budget = _host_i32(token_budget)
+        if self.h_token_budget.shape != (layout.total_chunks,):
+            raise DhsaError(2, "route_plan_tokens", "token_budget needs one entry per chunk")
+        self.h_row_ptr = np.zeros(layout.total_chunks + 1, np.int32)
+        nnz = ctypes.c_int64(0)
+        _check(lib.dhsa_route_plan_tokens(ctypes.byref(layout.struct), self.h_token_budget.ctypes.data,
+                                          self.h_row_ptr.ctypes.data, ctypes.byref(nnz)), "dhsa_route_plan_tokens")
+        self.nnz = int(nnz.value)
+        self.d_row_ptr = torch.from_numpy(self.h_row_ptr).to(layout.device)
+        self.d_token_budget = torch.from_numpy(self.h_token_budget).to(layout.device)
+
+
 def chunk_summarize(layout: Layout, q: torch.Tensor, k: torch.Tensor,
                     q_sum: Optional[torch.Tensor] = None, k_sum: Optional[torch.Tensor] = None
                     ) -> Tuple[torch.Tensor, torch.Tensor]:
@@ -219,6 +242,24 @@ def route(layout: Layout, plan: RoutePlan, q_sum: torch.Tensor, k_sum: torch.Ten
     return block_idx
 
 
+def route_tokens(layout: Layout, plan: TokenPlan, q_sum: torch.Tensor, k_sum: torch.Tensor,
+                 block_idx: Optional[torch.Tensor] = None, grouped: bool = False) -> torch.Tensor:
+    """Stage 2 under a token budget (dhsa_route_tokens): int32 [Hq, nnz], each row its kept chunks
+    ascending, the diagonal, then -1 up to the row's capacity."""
+    if not isinstance(plan, TokenPlan):
+        raise DhsaError(2, "route_tokens", "needs a TokenPlan")
+    if block_idx is None:
+        block_idx = torch.empty((layout.num_q_heads, plan.nnz), dtype=torch.int32, device=q_sum.device)
+    for t, name in ((q_sum, "q_sum"), (k_sum, "k_sum")):
+        if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
+            raise DhsaError(2, name, "expected a contiguous float32 GPU tensor")
+    _check(load_library().dhsa_route_tokens(ctypes.byref(layout.struct), _ptr(q_sum), _ptr(k_sum),
+                                            _ptr(plan.d_token_budget), plan.h_token_budget.ctypes.data,
+                                            _ptr(plan.d_row_ptr), plan.h_row_ptr.ctypes.data, plan.nnz,
+                                            int(bool(grouped)), _ptr(block_idx), _stream()), "dhsa_route_tokens")
+    return block_idx
+
+
 def sparse_prefill(layout: Layout, plan: RoutePlan, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                    block_idx: torch.Tensor, softmax_scale: Optional[float] = None, return_lse: bool = False,
                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
@@ -242,15 +283,23 @@ def sparse_prefill(layout: Layout, plan: RoutePlan, q: torch.Tensor, k: torch.Te
     return (out, lse) if return_lse else out
 
 
-def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens, cu_chunks, seq_chunk_start, topk,
-            softmax_scale: Optional[float] = None, return_lse: bool = False, grouped: bool = False):
-    """The whole path: summaries, routing (per query head, or per KV head when ``grouped``), sparse
-    attention.  Returns a dict of device tensors."""
+def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens, cu_chunks, seq_chunk_start, topk=None,
+            softmax_scale: Optional[float] = None, return_lse: bool = False, grouped: bool = False,
+            token_budget=None):
+    """The whole path: summaries, routing (per query head, or per KV head when ``grouped``; a chunk
+    budget ``topk`` or a token budget ``token_budget``, one entry per chunk), sparse attention.
+    Returns a dict of device tensors."""
+    if (topk is None) == (token_budget is None):
+        raise DhsaError(2, "prefill", "give exactly one of topk and token_budget")
     layout = Layout(cu_seqlens, cu_chunks, seq_chunk_start, q.shape[1], k.shape[1], q.shape[2], q.dtype,
                     device=q.device)
-    plan = RoutePlan(layout, topk)
     q_sum, k_sum = chunk_summarize(layout, q, k)
-    block_idx = route(layout, plan, q_sum, k_sum, grouped=grouped)
+    if token_budget is None:
+        plan = RoutePlan(layout, topk)
+        block_idx = route(layout, plan, q_sum, k_sum, grouped=grouped)
+    else:
+        plan = TokenPlan(layout, token_budget)
+        block_idx = route_tokens(layout, plan, q_sum, k_sum, grouped=grouped)
     res = sparse_prefill(layout, plan, q, k, v, block_idx, softmax_scale, return_lse=return_lse)
     out, lse = res if return_lse else (res, None)
     return dict(out=out, lse=lse, q_sum=q_sum, k_sum=k_sum, row_ptr=plan.h_row_ptr, block_idx=block_idx,

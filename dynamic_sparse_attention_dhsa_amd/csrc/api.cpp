@@ -3,6 +3,9 @@
 // synchronises; every failure is reported before any kernel is enqueued.
 #include <math.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "dhsa_internal.hpp"
 
 using dhsa::Plan;
@@ -136,6 +139,70 @@ dhsa_status check_seqlens(int32_t B, int32_t T, const int32_t* cu_seqlens, const
 }
 
 
+// Row capacities under a token budget: row i holds 1 + the number of the shortest earlier chunks
+// of its sequence whose lengths fit in h_tb[i] (the most any ranking could keep).  A Fenwick tree
+// over chunk lengths (counts and token sums) answers each row in O(log max_len).  Writes
+// h_row_ptr, or (h_row_ptr == nullptr) compares against h_check.  *too_wide: some row with more
+// candidates than the routing registers hold keeps some but not all of them.
+dhsa_status plan_tokens(const dhsa_layout* L, const int32_t* h_tb, int32_t* h_row_ptr, const int32_t* h_check,
+                        int64_t* nnz, bool* too_wide) {
+  const int32_t* sc = L->h_seq_chunk_start;
+  const int32_t* cc = L->h_cu_chunks;
+  for (int32_t c = 0; c < L->total_chunks; ++c)
+    if (h_tb[c] < 0) return DHSA_ERR_BAD_BUDGET;
+  int32_t maxlen = 1;
+  for (int32_t c = 0; c < L->total_chunks; ++c) maxlen = std::max(maxlen, cc[c + 1] - cc[c]);
+  int LOG = 1;
+  while ((1 << LOG) <= maxlen) ++LOG;
+  const int N = 1 << LOG;                         // tree positions 1..N-1 hold lengths 1..N-1
+  std::vector<int64_t> fcnt(N, 0), fsum(N, 0);
+  int64_t acc = 0;
+  if (h_row_ptr != nullptr) h_row_ptr[0] = 0;
+  else if (h_check[0] != 0) return DHSA_ERR_BAD_SHAPE;
+  *too_wide = false;
+  for (int32_t b = 0; b < L->num_seqs; ++b) {
+    std::fill(fcnt.begin(), fcnt.end(), 0);
+    std::fill(fsum.begin(), fsum.end(), 0);
+    int64_t total = 0;                            // tokens of the earlier chunks
+    for (int32_t c = sc[b]; c < sc[b + 1]; ++c) {
+      const int32_t i_loc = c - sc[b];
+      const int64_t budget = h_tb[c];
+      int64_t fit;
+      if (budget >= total) {
+        fit = i_loc;
+      } else {
+        // largest length bound v with sum(lengths <= v) <= budget, then part of the next length
+        int pos = 0;
+        int64_t cnt = 0, sum = 0;
+        for (int step = N >> 1; step > 0; step >>= 1) {
+          const int nx = pos + step;
+          if (nx < N && sum + fsum[nx] <= budget) {
+            pos = nx;
+            sum += fsum[nx];
+            cnt += fcnt[nx];
+          }
+        }
+        // chunks of length pos + 1 that still fit (all of that length would exceed the budget)
+        const int64_t v = pos + 1;
+        fit = cnt + (v < N ? (budget - sum) / v : 0);
+        if (i_loc > dhsa::kRouteRegCand) *too_wide = true;
+      }
+      acc += fit + 1;
+      if (acc > 0x7fffffffLL) return DHSA_ERR_BAD_SHAPE;
+      if (h_row_ptr != nullptr) h_row_ptr[c + 1] = (int32_t)acc;
+      else if (h_check[c + 1] != (int32_t)acc) return DHSA_ERR_BAD_SHAPE;
+      const int32_t len = cc[c + 1] - cc[c];
+      total += len;
+      for (int x = len; x < N; x += x & -x) {
+        fcnt[x] += 1;
+        fsum[x] += len;
+      }
+    }
+  }
+  *nnz = acc;
+  return DHSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -179,6 +246,15 @@ dhsa_status dhsa_route_plan(const dhsa_layout* layout, const int32_t* h_topk, in
   return DHSA_OK;
 }
 
+dhsa_status dhsa_route_plan_tokens(const dhsa_layout* layout, const int32_t* h_token_budget, int32_t* h_row_ptr,
+                                   int64_t* nnz) {
+  dhsa_status st = check_layout(layout, nullptr);
+  if (st != DHSA_OK) return st;
+  if (h_token_budget == nullptr || h_row_ptr == nullptr || nnz == nullptr) return DHSA_ERR_NULL_ARG;
+  bool too_wide = false;
+  return plan_tokens(layout, h_token_budget, h_row_ptr, nullptr, nnz, &too_wide);
+}
+
 dhsa_status dhsa_chunk_summarize(const dhsa_layout* layout, const void* q, const void* k, float* q_sum,
                                  float* k_sum, void* stream) {
   Plan p;
@@ -215,6 +291,27 @@ dhsa_status dhsa_route_grouped(const dhsa_layout* layout, const float* q_sum, co
                                const int32_t* row_ptr, const int32_t* h_row_ptr, int64_t nnz,
                                int32_t* block_idx, void* stream) {
   return route_common(layout, q_sum, k_sum, row_ptr, h_row_ptr, nnz, block_idx, true, stream);
+}
+
+dhsa_status dhsa_route_tokens(const dhsa_layout* layout, const float* q_sum, const float* k_sum,
+                              const int32_t* token_budget, const int32_t* h_token_budget, const int32_t* row_ptr,
+                              const int32_t* h_row_ptr, int64_t nnz, int32_t grouped, int32_t* block_idx,
+                              void* stream) {
+  Plan p;
+  dhsa_status st = check_layout(layout, &p);
+  if (st != DHSA_OK) return st;
+  if (h_token_budget == nullptr || h_row_ptr == nullptr) return DHSA_ERR_NULL_ARG;
+  int64_t planned = 0;
+  bool too_wide = false;
+  st = plan_tokens(layout, h_token_budget, nullptr, h_row_ptr, &planned, &too_wide);
+  if (st != DHSA_OK) return st;
+  if (planned != nnz) return DHSA_ERR_BAD_SHAPE;
+  if (too_wide) return DHSA_ERR_UNSUPPORTED;
+  if (p.C == 0) return DHSA_OK;
+  if (q_sum == nullptr || k_sum == nullptr || token_budget == nullptr || row_ptr == nullptr || block_idx == nullptr)
+    return DHSA_ERR_NULL_ARG;
+  return launched(dhsa::launch_route_tokens(p, q_sum, k_sum, token_budget, row_ptr, nnz, block_idx, grouped != 0,
+                                            (hipStream_t)stream));
 }
 
 dhsa_status dhsa_sparse_prefill(const dhsa_layout* layout, const void* q, const void* k, const void* v,

@@ -31,6 +31,11 @@ constexpr int kRouteRegCand = 1024;
 hipError_t launch_route(const Plan& p, const float* q_sum, const float* k_sum, const int32_t* row_ptr,
                         int64_t nnz, int32_t* block_idx, bool wide_rows, bool grouped, hipStream_t stream);
 
+// Stage 2 under a token budget (device token_budget [C]); rows sized by dhsa_route_plan_tokens.
+hipError_t launch_route_tokens(const Plan& p, const float* q_sum, const float* k_sum, const int32_t* token_budget,
+                               const int32_t* row_ptr, int64_t nnz, int32_t* block_idx, bool grouped,
+                               hipStream_t stream);
+
 // Stage 3: block-sparse causal prefill.
 hipError_t launch_prefill_bf16(const Plan& p, const void* q, const void* k, const void* v,
                                const int32_t* row_ptr, int64_t nnz, const int32_t* block_idx,

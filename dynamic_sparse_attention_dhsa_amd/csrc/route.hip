@@ -54,11 +54,14 @@ __device__ inline uint64_t rank_key(float s, int j) {
 
 __device__ inline int key_chunk(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
 
-template <int D, bool GROUPED>
+// TOKENS: the budget is token_budget[i] tokens instead of the row length (longest fitting prefix of
+// the ranking; the row's unused entries get -1).
+template <int D, bool GROUPED, bool TOKENS>
 __global__ __launch_bounds__(kWaves * 64) void route_kernel(
     const float* __restrict__ q_sum, const float* __restrict__ k_sum,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ seq_chunk_start,
-    int32_t* __restrict__ block_idx, int B, int C, int Hq, int Hkv, long long nnz) {
+    int32_t* __restrict__ block_idx, int B, int C, int Hq, int Hkv, long long nnz,
+    const int32_t* __restrict__ cu_chunks, const int32_t* __restrict__ token_budget) {
   __shared__ __attribute__((aligned(16))) float qs[kWaves][D];
   __shared__ float sc[kWaves][kRegCand];       // the four rows' scores
   const int nhb = (Hq + kWaves - 1) / kWaves;  // head blocks per chunk
@@ -79,7 +82,15 @@ __global__ __launch_bounds__(kWaves * 64) void route_kernel(
   const int kk = row_ptr[i + 1] - row_ptr[i] - 1;
   int32_t* out = block_idx + (size_t)h * nnz + row_ptr[i];
   // the same for every head of the chunk, so block-uniform
-  if (!(kk > 0 && kk < nc && nc <= kRegCand)) {
+  if constexpr (TOKENS) {
+    // every earlier chunk fits (the row then holds them all, ascending), or there is none
+    if (token_budget[i] >= cu_chunks[i] - cu_chunks[first]) {
+      for (int x = lane; x < nc; x += 64) out[x] = first + x;
+      if (lane == 0) out[nc] = i;
+      return;
+    }
+    if (nc > kRegCand) return;                 // refused on the host: more candidates than registers
+  } else if (!(kk > 0 && kk < nc && nc <= kRegCand)) {
     if (kk >= nc) {                            // every earlier chunk is kept
       for (int x = lane; x < nc; x += 64) out[x] = first + x;
       if (lane == 0) out[nc] = i;
@@ -167,8 +178,20 @@ __global__ __launch_bounds__(kWaves * 64) void route_kernel(
 #pragma unroll
   for (int b = 0; b < kRegBatches; ++b)
     ob[b] = (b < nb && 64 * b + lane < nc) ? ordered_bits(row[64 * b + lane]) : 0u;
-  sel::select_dispatch<1>(nb, ob, kk, first, lane, out);
-  if (lane == 0) out[kk] = i;
+  if constexpr (TOKENS) {
+    int len[kRegBatches];
+#pragma unroll
+    for (int b = 0; b < kRegBatches; ++b) {
+      const int j = first + 64 * b + lane;
+      len[b] = (b < nb && j < i) ? cu_chunks[j + 1] - cu_chunks[j] : 0;
+    }
+    const int m = sel::select_tokens_dispatch<1>(nb, ob, len, token_budget[i], first, lane, out);
+    for (int x = m + 1 + lane; x <= kk; x += 64) out[x] = -1;   // the row's unused capacity
+    if (lane == 0) out[m] = i;
+  } else {
+    sel::select_dispatch<1>(nb, ob, kk, first, lane, out);
+    if (lane == 0) out[kk] = i;
+  }
 }
 
 // General rows: more candidates than the main kernel holds in registers.
@@ -260,8 +283,8 @@ template <int D, bool GROUPED>
 hipError_t launch_route_d(const Plan& p, const float* q_sum, const float* k_sum, const int32_t* row_ptr,
                           int64_t nnz, int32_t* block_idx, bool wide_rows, hipStream_t stream) {
   dim3 grid(p.C * ((p.Hq + kWaves - 1) / kWaves));
-  hipLaunchKernelGGL((route_kernel<D, GROUPED>), grid, dim3(kWaves * 64), 0, stream, q_sum, k_sum, row_ptr,
-                     p.seq_chunk_start, block_idx, p.B, p.C, p.Hq, p.Hkv, (long long)nnz);
+  hipLaunchKernelGGL((route_kernel<D, GROUPED, false>), grid, dim3(kWaves * 64), 0, stream, q_sum, k_sum, row_ptr,
+                     p.seq_chunk_start, block_idx, p.B, p.C, p.Hq, p.Hkv, (long long)nnz, p.cu_chunks, nullptr);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !wide_rows) return err;
   hipLaunchKernelGGL((route_wide_kernel<D, GROUPED>), dim3(p.C, p.Hq), dim3(kWideThreads), 0, stream, q_sum,
@@ -276,7 +299,34 @@ hipError_t launch_route_g(const Plan& p, const float* q_sum, const float* k_sum,
                  : launch_route_d<D, false>(p, q_sum, k_sum, row_ptr, nnz, block_idx, wide_rows, stream);
 }
 
+template <int D>
+hipError_t launch_route_tokens_d(const Plan& p, const float* q_sum, const float* k_sum, const int32_t* token_budget,
+                                 const int32_t* row_ptr, int64_t nnz, int32_t* block_idx, bool grouped,
+                                 hipStream_t stream) {
+  dim3 grid(p.C * ((p.Hq + kWaves - 1) / kWaves));
+  if (grouped)
+    hipLaunchKernelGGL((route_kernel<D, true, true>), grid, dim3(kWaves * 64), 0, stream, q_sum, k_sum, row_ptr,
+                       p.seq_chunk_start, block_idx, p.B, p.C, p.Hq, p.Hkv, (long long)nnz, p.cu_chunks, token_budget);
+  else
+    hipLaunchKernelGGL((route_kernel<D, false, true>), grid, dim3(kWaves * 64), 0, stream, q_sum, k_sum, row_ptr,
+                       p.seq_chunk_start, block_idx, p.B, p.C, p.Hq, p.Hkv, (long long)nnz, p.cu_chunks, token_budget);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_route_tokens(const Plan& p, const float* q_sum, const float* k_sum, const int32_t* token_budget,
+                               const int32_t* row_ptr, int64_t nnz, int32_t* block_idx, bool grouped,
+                               hipStream_t stream) {
+  if (p.C == 0) return hipSuccess;
+  switch (p.d) {
+    case 32: return launch_route_tokens_d<32>(p, q_sum, k_sum, token_budget, row_ptr, nnz, block_idx, grouped, stream);
+    case 64: return launch_route_tokens_d<64>(p, q_sum, k_sum, token_budget, row_ptr, nnz, block_idx, grouped, stream);
+    case 128: return launch_route_tokens_d<128>(p, q_sum, k_sum, token_budget, row_ptr, nnz, block_idx, grouped, stream);
+    case 256: return launch_route_tokens_d<256>(p, q_sum, k_sum, token_budget, row_ptr, nnz, block_idx, grouped, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_route(const Plan& p, const float* q_sum, const float* k_sum, const int32_t* row_ptr,
                         int64_t nnz, int32_t* block_idx, bool wide_rows, bool grouped, hipStream_t stream) {

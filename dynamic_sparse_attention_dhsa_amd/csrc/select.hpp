@@ -67,5 +67,59 @@ __device__ inline void select_dispatch(int nb, const uint32_t (&ob)[kSelBatches]
   }
 }
 
+// Token-budget selection: keep the longest prefix of the (score desc, index asc) ranking whose lengths
+// (len[b] for candidate 64 b + lane, 0 for an empty slot) sum to at most `budget`.  With 64-bit keys
+// K = (ordered score bits << 32) | ~index (distinct; larger = better ranked; 0 marks an empty slot),
+// the kept set is {K >= X} for X the smallest value whose at-or-above length sum fits; X is found
+// bit by bit from the top: bit b stays 0 when the largest value with that bit 0 (lower bits all 1)
+// still fits.  Writes the kept indices ascending (first + 64 b + lane) and returns how many.
+__device__ inline int wave_sum_i32(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  x += __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  x += __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false);  // row_mirror
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
+template <int NB>
+__device__ inline int select_tokens_and_write(const uint32_t (&ob)[kSelBatches], const int (&len)[kSelBatches],
+                                              int budget, int first, int lane, int32_t* __restrict__ out) {
+  uint64_t key[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    key[b] = ob[b] ? (((uint64_t)ob[b] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(first + 64 * b + lane))) : 0ull;
+  uint64_t X = 0ull;
+  for (int bit = 63; bit >= 0; --bit) {
+    const uint64_t x1 = X | ((1ull << bit) - 1ull);
+    int part = 0;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) part += (key[b] != 0ull && key[b] >= x1) ? len[b] : 0;
+    if (wave_sum_i32(part) > budget) X |= 1ull << bit;
+  }
+  const uint64_t below = (1ull << lane) - 1ull;
+  int pos = 0;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const bool keep = key[b] != 0ull && key[b] >= X;
+    const uint64_t km = __ballot(keep);
+    if (keep) out[pos + __popcll(km & below)] = first + 64 * b + lane;
+    pos += __popcll(km);
+  }
+  return pos;
+}
+
+template <int NB>
+__device__ inline int select_tokens_dispatch(int nb, const uint32_t (&ob)[kSelBatches], const int (&len)[kSelBatches],
+                                             int budget, int first, int lane, int32_t* __restrict__ out) {
+  if constexpr (NB > kSelBatches) {
+    return 0;
+  } else {
+    if (nb == NB) return select_tokens_and_write<NB>(ob, len, budget, first, lane, out);
+    return select_tokens_dispatch<NB + 1>(nb, ob, len, budget, first, lane, out);
+  }
+}
+
 }  // namespace sel
 }  // namespace dhsa

@@ -138,6 +138,41 @@ dhsa_status dhsa_route_grouped(const dhsa_layout* layout, const float* q_sum, co
                                const int32_t* row_ptr, const int32_t* h_row_ptr, int64_t nnz,
                                int32_t* block_idx, void* stream);
 
+/* ---- Routing under a token budget (an extension: the pages keep the
+ * important token interactions - "Long-Context Modeling with Dynamic
+ * Hierarchical Sparse Attention for On-Device LLMs", Abstract - and report the
+ * memory saved, without fixing how much is kept; a budget in tokens is the
+ * other plain reading beside the chunk count).  Query chunk i ranks the earlier
+ * chunks of its sequence exactly as dhsa_route (score descending, chunk
+ * ascending) and keeps the longest prefix of that ranking whose chunk lengths
+ * sum to at most token_budget[i] (the first chunk that does not fit ends it),
+ * plus itself. */
+
+/* Plan (host only, pure).  The kept count depends on the scores, so row i gets
+ * the most any ranking could keep: 1 + how many of the shortest earlier chunks
+ * of the sequence fit in h_token_budget[i].
+ *   h_token_budget  host [C] tokens per query chunk (>= 0, else BAD_BUDGET)
+ *   h_row_ptr       host [C+1] written: CSR row offsets, shared by all q heads
+ *   nnz             written: h_row_ptr[C] */
+dhsa_status dhsa_route_plan_tokens(const dhsa_layout* layout, const int32_t* h_token_budget,
+                                   int32_t* h_row_ptr, int64_t* nnz);
+
+/* Routing under a token budget, per q head (grouped = 0) or per KV head with
+ * the group sum of the query summaries (grouped != 0, as dhsa_route_grouped).
+ * Row (h, i) gets its kept chunks ascending, then i, then -1 up to the row's
+ * capacity; dhsa_sparse_prefill skips the -1 entries.
+ *   token_budget    device [C], equal to its host mirror h_token_budget
+ *   row_ptr         device [C+1] from dhsa_route_plan_tokens with the same
+ *                   budgets; h_row_ptr its host mirror (checked against the plan:
+ *                   BAD_SHAPE if it differs, or if nnz does)
+ *   block_idx       device [Hq, nnz] int32, written completely
+ * UNSUPPORTED when a row with more than 1024 earlier chunks in its sequence
+ * keeps some but not all of them. */
+dhsa_status dhsa_route_tokens(const dhsa_layout* layout, const float* q_sum, const float* k_sum,
+                              const int32_t* token_budget, const int32_t* h_token_budget,
+                              const int32_t* row_ptr, const int32_t* h_row_ptr, int64_t nnz,
+                              int32_t grouped, int32_t* block_idx, void* stream);
+
 /* Stage 3: block-sparse causal prefill (ICML 2026 page, Abstract: tiled
  * backend; exact softmax over the kept token interactions).  Query token t of
  * chunk i, head h attends to every key u <= t lying in a kept chunk of row
@@ -147,7 +182,8 @@ dhsa_status dhsa_route_grouped(const dhsa_layout* layout, const float* q_sum, co
  * fp32 accumulation; out is rounded to its dtype (bf16: to nearest even).
  *   row_ptr, block_idx  device CSR as written by dhsa_route (or any list in the
  *              same format: ascending, inside the query chunk's sequence, j <= i,
- *              with the diagonal present)
+ *              with the diagonal present; entries outside the sequence's chunks
+ *              up to i, such as the -1 padding of dhsa_route_tokens, are skipped)
  *   lse        device [Hq, T] float32 or NULL
  * out (and lse) are written completely.  bf16 additionally needs k and v below
  * 2 GiB each (T * Hkv * head_dim * 2 bytes): larger returns UNSUPPORTED. */

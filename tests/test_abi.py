@@ -130,6 +130,68 @@ def test_route_plan_matches_budget_rule():
     assert lib.dhsa_route_plan(m.ref(), None, rp.ctypes.data, ctypes.byref(nnz)) == NULL
 
 
+def test_route_plan_tokens_matches_oracle_plan():
+    """Host-only token-budget plan against the oracle's (which is pinned by a sorted()-based brute
+    force): random lengths, budgets from 0 to past the whole prefix, several sequences."""
+    import oracle
+    lib = Bd.load_library()
+    rng = np.random.default_rng(7)
+    for trial in range(40):
+        lens = [rng.integers(1, 40, size=int(rng.integers(0, 30))) for _ in range(int(rng.integers(1, 4)))]
+        cc, sc, cs = [0], [0], [0]
+        for L in lens:
+            for n in L:
+                cc.append(cc[-1] + int(n))
+            sc.append(sc[-1] + len(L))
+            cs.append(cc[-1])
+        C = sc[-1]
+        m = Mirror(cs, cc, sc)
+        tb = rng.integers(0, 400 if trial % 2 else 60, size=C).astype(np.int32)
+        rp = np.zeros(C + 1, np.int32)
+        nnz = ctypes.c_int64()
+        assert lib.dhsa_route_plan_tokens(m.ref(), tb.ctypes.data, rp.ctypes.data, ctypes.byref(nnz)) == OK
+        rp_o, nnz_o = oracle.route_plan_tokens(np.asarray(cc), np.asarray(sc), tb)
+        assert rp.tolist() == rp_o.tolist() and nnz.value == nnz_o, trial
+
+
+def test_route_tokens_rejects_before_launch():
+    lib = Bd.load_library()
+    m = Mirror(*GOOD)          # chunk lengths 4, 6 | 3, 4
+    tb = np.array([0, 5, 3, 2], np.int32)
+    rp = np.zeros(5, np.int32)
+    nnz = ctypes.c_int64()
+    assert lib.dhsa_route_plan_tokens(m.ref(), tb.ctypes.data, rp.ctypes.data, ctypes.byref(nnz)) == OK
+    assert rp.tolist() == [0, 1, 3, 4, 5] and nnz.value == 5
+    # the row pointers must be the plan of the same budgets, and nnz its total
+    assert lib.dhsa_route_tokens(m.ref(), None, FAKE, FAKE, tb.ctypes.data, FAKE, rp.ctypes.data, 5, 0, FAKE,
+                                 None) == NULL
+    assert lib.dhsa_route_tokens(m.ref(), FAKE, FAKE, FAKE, tb.ctypes.data, FAKE, rp.ctypes.data, 6, 0, FAKE,
+                                 None) == SHAPE
+    tb2 = tb.copy()
+    tb2[3] = 4                 # row 3 could now hold chunk 2 as well
+    assert lib.dhsa_route_tokens(m.ref(), FAKE, FAKE, FAKE, tb2.ctypes.data, FAKE, rp.ctypes.data, 5, 0, FAKE,
+                                 None) == SHAPE
+    tb2[3] = -1
+    assert lib.dhsa_route_tokens(m.ref(), FAKE, FAKE, FAKE, tb2.ctypes.data, FAKE, rp.ctypes.data, 5, 0, FAKE,
+                                 None) == BUDGET
+    assert lib.dhsa_route_tokens(m.ref(), FAKE, FAKE, FAKE, None, FAKE, rp.ctypes.data, 5, 0, FAKE, None) == NULL
+    assert lib.dhsa_route_plan_tokens(m.ref(), tb2.ctypes.data, rp.ctypes.data, ctypes.byref(nnz)) == BUDGET
+    # more than 1024 candidates: only a budget that keeps them all is supported
+    n = 1100
+    cc = np.arange(n + 1, dtype=np.int32)
+    w = Mirror([0, n], cc, [0, n])
+    rpw = np.zeros(n + 1, np.int32)
+    full = np.arange(n, dtype=np.int32)          # every earlier chunk (length 1) fits
+    assert lib.dhsa_route_plan_tokens(w.ref(), full.ctypes.data, rpw.ctypes.data, ctypes.byref(nnz)) == OK
+    assert lib.dhsa_route_tokens(w.ref(), None, FAKE, FAKE, full.ctypes.data, FAKE, rpw.ctypes.data, nnz.value, 1,
+                                 FAKE, None) == NULL
+    part = full.copy()
+    part[-1] = 5
+    assert lib.dhsa_route_plan_tokens(w.ref(), part.ctypes.data, rpw.ctypes.data, ctypes.byref(nnz)) == OK
+    assert lib.dhsa_route_tokens(w.ref(), FAKE, FAKE, FAKE, part.ctypes.data, FAKE, rpw.ctypes.data, nnz.value, 1,
+                                 FAKE, None) == UNSUP
+
+
 def test_stage_calls_reject_before_launch():
     lib = Bd.load_library()
     m = Mirror(*GOOD)
