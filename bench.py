@@ -185,15 +185,18 @@ def decode_measure(torch, D, w, q, k, v, batch: int, steps: int = 30, warmup: in
     lay = D.Layout(cu_b, cc_b, scs_b, Hq, Hkv, d, q.dtype)
     st = D.DecodeState(batch, Hq, Hkv, d, q.dtype, T + warmup + steps + 1, 1024)
     st.load_prefix(lay, q[:T].repeat(batch, 1, 1), k[:T].repeat(batch, 1, 1), v[:T].repeat(batch, 1, 1))
-    # new tokens: rows of the sequence's last chunk, so the open chunk keeps growing with its topic
+    # new tokens: rows of the sequence's last chunk, so the open chunk keeps growing with its topic;
+    # every step's inputs are built (resident in HBM) before anything is timed
     src = torch.arange(T - 64, T, device=q.device)
     kept = torch.empty((batch, Hq, topk), dtype=torch.int32, device=q.device)
     out = torch.empty((batch, Hq, d), dtype=q.dtype, device=q.device)
+    idx = src[torch.arange(warmup + steps, device=q.device) % 64]
+    q_in = q[idx].unsqueeze(1).expand(-1, batch, -1, -1).contiguous()     # [steps, batch, Hq, d]
+    k_in = k[idx].unsqueeze(1).expand(-1, batch, -1, -1).contiguous()
+    v_in = v[idx].unsqueeze(1).expand(-1, batch, -1, -1).contiguous()
 
     def step(i):
-        r = src[i % 64].repeat(batch)
-        st.step(q[r].contiguous(), k[r].contiguous(), v[r].contiguous(), lo, hi, tau, topk, True, w.softmax_scale,
-                out=out, kept=kept)
+        st.step(q_in[i], k_in[i], v_in[i], lo, hi, tau, topk, True, w.softmax_scale, out=out, kept=kept)
 
     for i in range(warmup):
         step(i)

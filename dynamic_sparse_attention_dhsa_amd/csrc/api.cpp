@@ -110,19 +110,17 @@ dhsa_status check_decode_state(const dhsa_decode_state* st, dhsa::DecodeDims* di
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace layout of a decode step: spans, span counts, token counts, split-K partial states.
+// Workspace layout of a decode step: the kept tokens' cache rows, token counts, split-K partial states.
 size_t decode_workspace(const dhsa::DecodeDims& p, int topk, bool grouped, dhsa::DecodeWork* w, void* base) {
   const size_t rows = (size_t)p.B * (grouped ? p.Hkv : p.Hq);
   const int NS = (p.L + dhsa::kDecodeSlice - 1) / dhsa::kDecodeSlice;
-  const size_t o_spans = 0;
-  const size_t o_nspan = align256(o_spans + rows * (topk + 1) * sizeof(int4));
-  const size_t o_ntok = align256(o_nspan + rows * sizeof(int32_t));
+  const size_t o_urow = 0;
+  const size_t o_ntok = align256(o_urow + rows * (size_t)p.L * sizeof(int32_t));
   const size_t o_part = align256(o_ntok + rows * sizeof(int32_t));
   const size_t total = align256(o_part + (size_t)p.B * p.Hq * NS * (p.d + 2) * sizeof(float));
   if (w != nullptr) {
     char* c = (char*)base;
-    *w = dhsa::DecodeWork{(int4*)(c + o_spans), (int32_t*)(c + o_nspan), (int32_t*)(c + o_ntok),
-                          (float*)(c + o_part), NS};
+    *w = dhsa::DecodeWork{(int32_t*)(c + o_urow), (int32_t*)(c + o_ntok), (float*)(c + o_part), NS};
   }
   return total;
 }

@@ -34,6 +34,8 @@
 namespace dhsa {
 namespace {
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kAppendThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -148,30 +150,45 @@ __global__ __launch_bounds__(kAppendThreads) void decode_append_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------- route
+// Sum over the LS consecutive lanes that read one summary row (LS in {16, 32, 64}) on the DPP paths;
+// lane LS - 1 of each group holds the sum.
+template <int LS>
+__device__ inline float row_sum(float x) {
+  x += dpp_get<0xB1, 0xF>(x, 0.f);
+  x += dpp_get<0x4E, 0xF>(x, 0.f);
+  x += dpp_get<0x141, 0xF>(x, 0.f);
+  x += dpp_get<0x140, 0xF>(x, 0.f);
+  if constexpr (LS >= 32) x += dpp_get<0x142, 0xA>(x, 0.f);
+  if constexpr (LS >= 64) x += dpp_get<0x143, 0xC>(x, 0.f);
+  return x;
+}
+
 // One workgroup (kRouteThreads) per (sequence, row); a row is a q head, or a KV head when routing per
-// KV head.  Every thread scores closed chunks (stride kRouteThreads) into LDS; wave 0 then holds the
-// scores in registers, selects the top-k and writes the row's kept spans (closed chunks ascending, then
-// the open chunk) as int4 (first token, length, tokens before this span, 0), their count and the row's
-// total kept tokens.
-constexpr int kRouteThreads = 256;
+// KV head.  Each wave scores a contiguous range of closed chunks into LDS, reading the key summaries
+// across lanes; wave 0 then holds the scores in registers, selects the top-k and lays out the row's
+// kept spans (closed chunks ascending, then the open chunk) with their token offsets; every wave then
+// writes the spans' cache rows into the row array, and wave 0 the row's total kept tokens.
+constexpr int kRouteThreads = 1024;
 
 template <int D, bool GROUPED>
 __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(
     const float* __restrict__ q_run, const float* __restrict__ k_sum, const int32_t* __restrict__ seq_len,
     const int32_t* __restrict__ num_closed, const int32_t* __restrict__ chunk_start,
-    const int32_t* __restrict__ status, int Hq, int Hkv, int Cmax, int topk, int4* __restrict__ spans,
-    int32_t* __restrict__ nspan, int32_t* __restrict__ ntok, int32_t* __restrict__ kept_out) {
+    const int32_t* __restrict__ status, int Hq, int Hkv, int Cmax, int L, int topk, int32_t* __restrict__ urow,
+    int32_t* __restrict__ ntok, int32_t* __restrict__ kept_out) {
   __shared__ __attribute__((aligned(16))) float qv[D];
   __shared__ float scores[sel::kSelCand];
   __shared__ int32_t kl[sel::kSelCand];
+  __shared__ int3 span_lds[sel::kSelCand + 1];
+  __shared__ int32_t cs_l[sel::kSelCand + 1];    // chunk starts of the sequence, closed chunks then c0
   const int R = GROUPED ? Hkv : Hq;
   const int b = blockIdx.x / R, r = blockIdx.x % R, tid = threadIdx.x, lane = tid & 63;
   const int G = Hq / Hkv;
   const int g = GROUPED ? r : r / G;
   const size_t row = (size_t)b * R + r;
-  int4* sp = spans + row * (topk + 1);
+  int32_t* ur = urow + row * (size_t)L;
   if (status[b] != 0) {                           // stopped sequence: nothing to attend (block-uniform)
-    if (tid == 0) { nspan[row] = 0; ntok[row] = 0; }
+    if (tid == 0) ntok[row] = 0;
     return;
   }
   const int t_end = seq_len[b];                   // tokens in the cache, the new one included
@@ -179,6 +196,7 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(
   const int32_t* cs = chunk_start + (size_t)b * (Cmax + 1);
   const int c0 = cs[nc];
   const float inv = 1.0f / sqrtf((float)(t_end - c0));
+  for (int x = tid; x <= nc; x += kRouteThreads) cs_l[x] = cs[x];   // nc <= kDecodeMaxChunks
   for (int x = tid; x < D; x += kRouteThreads) {
     float a;
     if constexpr (GROUPED) {
@@ -192,61 +210,81 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(
   __syncthreads();
   const int kk = min(topk, nc);
   if (kk < nc && kk > 0) {
-    for (int j = tid; j < nc; j += kRouteThreads) {
-      const float4* kr = reinterpret_cast<const float4*>(k_sum + (((size_t)b * Cmax + j) * Hkv + g) * D);
-      float acc = 0.f;
-#pragma unroll 8
-      for (int x = 0; x < D / 4; ++x) {
-        const float4 kv = kr[x];
-        const float4 q4 = *reinterpret_cast<const float4*>(&qv[4 * x]);
-        acc = fmaf(q4.x, kv.x, acc);
-        acc = fmaf(q4.y, kv.y, acc);
-        acc = fmaf(q4.z, kv.z, acc);
-        acc = fmaf(q4.w, kv.w, acc);
+    // key summaries read across lanes: LS lanes x 16 bytes per summary row, RS rows per load, 16
+    // loads in flight per wave; each lane's partial dot product summed over its row's lanes
+    constexpr int LS = D / 4, RS = 64 / LS;
+    const int wv = tid >> 6, sr = lane / LS, sp = lane % LS;
+    const float4 q4 = *reinterpret_cast<const float4*>(&qv[4 * sp]);
+    const int per_wave = (nc + kRouteThreads / 64 - 1) / (kRouteThreads / 64);
+    const int j_lo = wv * per_wave, j_hi = min(nc, j_lo + per_wave);
+    for (int j0 = j_lo; j0 < j_hi; j0 += 16 * RS) {
+      float4 kv[16];
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int j = j0 + x * RS + sr;
+        kv[x] = j < j_hi ? *reinterpret_cast<const float4*>(k_sum + (((size_t)b * Cmax + j) * Hkv + g) * D + 4 * sp)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
       }
-      scores[j] = acc;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        float a = q4.x * kv[x].x;
+        a = fmaf(q4.y, kv[x].y, a);
+        a = fmaf(q4.z, kv[x].z, a);
+        a = fmaf(q4.w, kv[x].w, a);
+        a = row_sum<LS>(a);
+        const int j = j0 + x * RS + sr;
+        if (sp == LS - 1 && j < j_hi) scores[j] = a;
+      }
     }
   }
   __syncthreads();
-  if (tid >= 64) return;                          // wave 0 selects and writes
-  if (kk == nc) {
-    for (int x = lane; x < nc; x += 64) kl[x] = x;
-  } else if (kk > 0) {
-    uint32_t ob[sel::kSelBatches];
-    const int nb = (nc + 63) >> 6;
+  if (tid < 64) {                                 // wave 0 selects
+    if (kk == nc) {
+      for (int x = lane; x < nc; x += 64) kl[x] = x;
+    } else if (kk > 0) {
+      uint32_t ob[sel::kSelBatches];
+      const int nb = (nc + 63) >> 6;
 #pragma unroll
-    for (int bt = 0; bt < sel::kSelBatches; ++bt) {
-      const int j = 64 * bt + lane;
-      ob[bt] = (bt < nb && j < nc) ? sel::ordered_bits(scores[j]) : 0u;
+      for (int bt = 0; bt < sel::kSelBatches; ++bt) {
+        const int j = 64 * bt + lane;
+        ob[bt] = (bt < nb && j < nc) ? sel::ordered_bits(scores[j]) : 0u;
+      }
+      sel::select_dispatch<1>(nb, ob, kk, 0, lane, kl);
     }
-    sel::select_dispatch<1>(nb, ob, kk, 0, lane, kl);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  // spans with exclusive token offsets (a wave scan per 64 spans, carried across batches)
-  int carry = 0;
-  for (int base = 0; base <= kk; base += 64) {
-    const int i = base + lane;
-    int start = 0, len = 0;
-    if (i < kk) {
-      const int j = kl[i];
-      start = cs[j];
-      len = cs[j + 1] - start;
-    } else if (i == kk) {
-      start = c0;
-      len = t_end - c0;
-    }
-    int incl = len;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // spans with exclusive token offsets (a wave scan per 64 spans, carried across batches)
+    int carry = 0;
+    for (int base = 0; base <= kk; base += 64) {
+      const int i = base + lane;
+      int start = 0, len = 0;
+      if (i < kk) {
+        const int j = kl[i];
+        start = cs_l[j];
+        len = cs_l[j + 1] - start;
+      } else if (i == kk) {
+        start = c0;
+        len = t_end - c0;
+      }
+      int incl = len;
 #pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      const int o = __shfl_up(incl, m);
-      if (lane >= m) incl += o;
+      for (int m = 1; m < 64; m <<= 1) {
+        const int o = __shfl_up(incl, m);
+        if (lane >= m) incl += o;
+      }
+      if (i <= kk) span_lds[i] = make_int3(start, len, carry + incl - len);
+      carry += __shfl(incl, 63);
     }
-    if (i <= kk) sp[i] = make_int4(start, len, carry + incl - len, 0);
-    carry += __shfl(incl, 63);
+    if (lane == 0) ntok[row] = carry;
   }
-  if (lane == 0) { nspan[row] = kk + 1; ntok[row] = carry; }
+  __syncthreads();
+  // each span's tokens get their cache rows in the row array, in kept order (a wave per span)
+  for (int i = tid >> 6; i <= kk; i += kRouteThreads / 64) {
+    const int3 sp3 = span_lds[i];
+    for (int y = lane; y < sp3.y; y += 64) ur[sp3.z + y] = sp3.x + y;
+  }
+  if (tid >= 64) return;
   if (kept_out != nullptr) {                      // the kept closed chunks of every q head of the row
     const int h0 = GROUPED ? g * G : r, nh = GROUPED ? G : 1;
     for (int hh = 0; hh < nh; ++hh)
@@ -256,165 +294,296 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------- attend
-// One wave per (sequence, block of GH q heads sharing a kept row, slice of kDecodeSlice kept tokens):
-// GH = the group when routing per KV head (its heads read each K/V row once), else 1.  Per 64 tokens
-// (one per lane): the lane's key row against the GH queries, an online softmax per head in base 2,
-// then PV with 16-byte value loads (RPI rows per instruction, each lane 8 columns of one row).
+// Sum over the LPR consecutive lanes that read one key row (LPR in {8, 16, 32}) on the DPP paths:
+// quad permutes, the half-row mirror (8 lanes), the row mirror (16 lanes), then the broadcast of each
+// row's lane 15 into the next row (32 lanes: rows 1 and 3).  Lane LPR - 1 of each group holds the sum.
+template <int LPR>
+__device__ inline float group_sum(float x) {
+  x += dpp_get<0xB1, 0xF>(x, 0.f);
+  x += dpp_get<0x4E, 0xF>(x, 0.f);
+  x += dpp_get<0x141, 0xF>(x, 0.f);
+  if constexpr (LPR >= 16) x += dpp_get<0x140, 0xF>(x, 0.f);
+  if constexpr (LPR >= 32) x += dpp_get<0x142, 0xA>(x, 0.f);
+  return x;
+}
+
+// Split-K attention.  A wave owns (sequence, block of GH q heads sharing a kept row, slices s, s + S,
+// s + 2S, ... of kDecodeSlice kept tokens, S = the grid's slices per row): GH = the group when
+// routing per KV head (its heads read each K/V row once), else 1.  The kept tokens' cache rows come
+// from the routing kernel's row array, loaded once per slice.  Per block of 64 tokens:
+//   scores  K rows read across lanes (LPR lanes x 16 bytes per row, RPI rows per instruction, all of
+//           a block's loads in flight, the next block's issued with this block's values), each lane's
+//           partial dot products summed over its row's lanes on the DPP paths, the row's scores
+//           handed through LDS to the token's lane.  bf16: packed dot products of the unscaled
+//           queries with the keys as loaded (exact products, fp32 sums), the scale applied to the
+//           score, as the prefill kernel does;
+//   softmax online per head in base 2, one token per lane; bf16: weights rounded to bf16, and the
+//           normaliser sums the rounded weights;
+//   PV      16-byte value loads, RPV rows per instruction, each lane 8 columns of one row; bf16: two
+//           rows' values repacked into per-column pairs against the two tokens' weights.
 // Partial state per (sequence, q head, slice): (m, l, o[D]), o not normalised.
 template <typename T, int D, bool GROUPED, int GH>
 __global__ __launch_bounds__(64) void decode_attend_kernel(
     const T* __restrict__ q, const T* __restrict__ k_cache, const T* __restrict__ v_cache,
-    const int4* __restrict__ spans, const int32_t* __restrict__ nspan, const int32_t* __restrict__ ntok,
-    int Hq, int Hkv, int L, int topk, int NS, float scale_log2, float* __restrict__ part) {
-  constexpr int VEC = 16 / sizeof(T);             // elements per 16-byte load
+    const int32_t* __restrict__ urow, const int32_t* __restrict__ ntok, int Hq, int Hkv, int L, int NSg, int NS,
+    float scale_log2, float* __restrict__ part) {
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int EPL = 16 / sizeof(T);             // elements per 16-byte load
+  constexpr int LPR = D / EPL;                    // lanes per key row
+  constexpr int RPI = 64 / LPR;                   // key rows per load instruction
+  constexpr int NI = 64 / RPI;                    // load instructions per 64-row block
+  constexpr int KB = NI < 16 ? NI : 16;           // key loads in flight
   constexpr int PARTS = D / 8;                    // 8-element parts of a value row
-  constexpr int RPI = 64 / PARTS;                 // value rows per load instruction
-  __shared__ float qs[GH][D];
+  constexpr int RPV = 64 / PARTS;                 // value rows per load instruction
+  constexpr int NJV = 64 / RPV;                   // value row steps per 64-row block
+  constexpr int VW = 8 / EPL;                     // 16-byte loads per lane and value row (8 columns)
+  constexpr int VJB = NJV * VW <= 16 ? NJV : 16 / VW;   // value row steps in flight
+  constexpr int NB = kDecodeSlice / 64;           // blocks per slice
+  static_assert(LPR == 8 || LPR == 16 || LPR == 32, "key rows of 128, 256 or 512 bytes");
+  static_assert(VJB % 2 == 0, "value rows are taken in pairs");
+  __shared__ float qs[BF ? 1 : GH][D];
   __shared__ float pbuf[GH][64];
-  __shared__ int rowbuf[64];
+  __shared__ __attribute__((aligned(16))) float scb[64][GH];
+  __shared__ int rowbuf[NB][64];
   __shared__ float ored[64][9];
   const int lane = threadIdx.x;
-  const int s = blockIdx.x % NS;
-  const int bhb = blockIdx.x / NS;
+  const int s0 = blockIdx.x % NSg;
+  const int bhb = blockIdx.x / NSg;
   const int nhb = Hq / GH;
   const int b = bhb / nhb, h0 = (bhb % nhb) * GH;
   const int G = Hq / Hkv, g = h0 / G;
   const size_t row = (size_t)b * (GROUPED ? Hkv : Hq) + (GROUPED ? g : h0);
   const int n = ntok[row];
-  const int lo_tok = s * kDecodeSlice;
-  if (lo_tok >= n) return;                        // the combine reads only slices below n
-  const int hi_tok = min(n, lo_tok + kDecodeSlice);
-  const int ns = nspan[row];
-  const int4* sp = spans + row * (topk + 1);
-  for (int x = lane; x < GH * D; x += 64)
-    qs[x / D][x % D] = to_f(q[((size_t)b * Hq + h0 + x / D) * D + x % D]) * scale_log2;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  if (s0 * kDecodeSlice >= n) return;             // the combine reads only slices below n
   const T* kb = k_cache + ((size_t)b * L * Hkv + g) * D;      // row u at kb + u * Hkv * D
   const T* vb = v_cache + ((size_t)b * L * Hkv + g) * D;
   const size_t rs = (size_t)Hkv * D;
-  float m[GH], l[GH], o[GH][8];
-#pragma unroll
-  for (int hh = 0; hh < GH; ++hh) {
-    m[hh] = -INFINITY;
-    l[hh] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
-  }
-  const int rg = lane / PARTS, pt = lane % PARTS;
-  int span_hint = 0;
-  for (int blk = lo_tok; blk < hi_tok; blk += 64) {
-    const int tok = blk + lane;
-    const bool valid = tok < hi_tok;
-    // the span holding tok: the last span whose offset is <= tok (binary search from the block's first)
-    int lo_s = span_hint, hi_s = ns - 1;
-    while (lo_s < hi_s) {
-      const int mid = (lo_s + hi_s + 1) >> 1;
-      if (sp[mid].z <= tok) lo_s = mid; else hi_s = mid - 1;
-    }
-    const int4 spn = sp[lo_s];
-    const int u = spn.x + (tok - spn.z);
-    span_hint = __builtin_amdgcn_readfirstlane(lo_s);   // lane 0 holds the block's lowest token
-    float sc[GH];
-#pragma unroll
-    for (int hh = 0; hh < GH; ++hh) sc[hh] = -INFINITY;
-    if (valid) {
-      const uint4* kr = reinterpret_cast<const uint4*>(kb + (size_t)u * rs);
-      float acc[GH];
-#pragma unroll
-      for (int hh = 0; hh < GH; ++hh) acc[hh] = 0.f;
-#pragma unroll 4
-      for (int x = 0; x < D / VEC; ++x) {
-        const uint4 raw = kr[x];
-        float kf[VEC];
-        if constexpr (VEC == 8) {
-          const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            kf[2 * e] = __uint_as_float(w[e] << 16);
-            kf[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-          }
-        } else {
-          kf[0] = __uint_as_float(raw.x); kf[1] = __uint_as_float(raw.y);
-          kf[2] = __uint_as_float(raw.z); kf[3] = __uint_as_float(raw.w);
-        }
-#pragma unroll
-        for (int hh = 0; hh < GH; ++hh)
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) acc[hh] = fmaf(qs[hh][x * VEC + e], kf[e], acc[hh]);
-      }
-#pragma unroll
-      for (int hh = 0; hh < GH; ++hh) sc[hh] = acc[hh];
-    }
-    rowbuf[lane] = valid ? u : -1;
+  const int32_t* ur = urow + row * (size_t)L;
+  const int kr = lane / LPR, kp = lane % LPR;     // key row within an instruction, piece of the row
+  const int vg = lane / PARTS, vp = lane % PARTS; // value row within an instruction, part of the row
+  // this lane's slice of the queries, elements kp * EPL .. + EPL of every head: bf16 pairs as
+  // stored (bf16), or scaled floats (fp32)
+  uint32_t qpk[GH][4];
+  float qreg[GH][EPL];
+  if constexpr (BF) {
 #pragma unroll
     for (int hh = 0; hh < GH; ++hh) {
-      const float m_new = fmaxf(m[hh], wave_max(sc[hh]));
-      const float alpha = exp2f(m[hh] - m_new);   // m = -inf on the first block: alpha = 0
-      const float p = valid ? exp2f(sc[hh] - m_new) : 0.f;
-      l[hh] = l[hh] * alpha + wave_add(p);
+      const uint4 w = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + h0 + hh) * D + kp * EPL);
+      qpk[hh][0] = w.x; qpk[hh][1] = w.y; qpk[hh][2] = w.z; qpk[hh][3] = w.w;
+    }
+  } else {
+    for (int x = lane; x < GH * D; x += 64)
+      qs[x / D][x % D] = to_f(q[((size_t)b * Hq + h0 + x / D) * D + x % D]) * scale_log2;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[hh][e] *= alpha;
-      m[hh] = m_new;
-      pbuf[hh][lane] = p;
+    for (int hh = 0; hh < GH; ++hh)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qreg[hh][e] = qs[hh][kp * EPL + e];
+  }
+
+  for (int s = s0; s * kDecodeSlice < n; s += NSg) {
+    const int lo_tok = s * kDecodeSlice;
+    const int hi_tok = min(n, lo_tok + kDecodeSlice);
+    float m[GH], l[GH], o[GH][8];
+#pragma unroll
+    for (int hh = 0; hh < GH; ++hh) {
+      m[hh] = -INFINITY;
+      l[hh] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
+    }
+    // the slice's cache rows (-1 past its end), one load per block
+#pragma unroll
+    for (int bk = 0; bk < NB; ++bk) {
+      const int t = lo_tok + 64 * bk + lane;
+      rowbuf[bk][lane] = t < hi_tok ? ur[t] : -1;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-#pragma unroll 4
-    for (int j = 0; j < 64 / RPI; ++j) {
-      const int tt = j * RPI + rg;
-      const int vr = rowbuf[tt];
-      if (vr >= 0) {
-        const T* vp = vb + (size_t)vr * rs + pt * 8;
-        float vf[8];
-        if constexpr (VEC == 8) {
-          const uint4 raw = *reinterpret_cast<const uint4*>(vp);
-          const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    const int nblk = (hi_tok - lo_tok + 63) / 64;
+    uint4 kraw[KB];
+    auto issue_k = [&](int bk, int j0) __attribute__((always_inline)) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            vf[2 * e] = __uint_as_float(w[e] << 16);
-            vf[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+      for (int jj = 0; jj < KB; ++jj) {
+        const int u = rowbuf[bk][(j0 + jj) * RPI + kr];
+        kraw[jj] = u >= 0 ? *reinterpret_cast<const uint4*>(kb + (size_t)u * rs + kp * EPL) : make_uint4(0, 0, 0, 0);
+      }
+    };
+    auto score_k = [&](int j0) __attribute__((always_inline)) {
+#pragma unroll
+      for (int jj = 0; jj < KB; ++jj) {
+        float acc[GH];
+        if constexpr (BF) {
+          const uint32_t kw[4] = {kraw[jj].x, kraw[jj].y, kraw[jj].z, kraw[jj].w};
+#pragma unroll
+          for (int hh = 0; hh < GH; ++hh) {
+            float a = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kw[e]), __builtin_bit_cast(bf16x2, qpk[hh][e]),
+                                                  a, false);
+            acc[hh] = a;
           }
         } else {
-          const uint4 r0 = *reinterpret_cast<const uint4*>(vp);
-          const uint4 r1 = *reinterpret_cast<const uint4*>(vp + 4);
-          vf[0] = __uint_as_float(r0.x); vf[1] = __uint_as_float(r0.y); vf[2] = __uint_as_float(r0.z);
-          vf[3] = __uint_as_float(r0.w); vf[4] = __uint_as_float(r1.x); vf[5] = __uint_as_float(r1.y);
-          vf[6] = __uint_as_float(r1.z); vf[7] = __uint_as_float(r1.w);
+          const float kf[4] = {__uint_as_float(kraw[jj].x), __uint_as_float(kraw[jj].y),
+                               __uint_as_float(kraw[jj].z), __uint_as_float(kraw[jj].w)};
+#pragma unroll
+          for (int hh = 0; hh < GH; ++hh) {
+            float a = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a = fmaf(qreg[hh][e], kf[e], a);
+            acc[hh] = a;
+          }
         }
 #pragma unroll
-        for (int hh = 0; hh < GH; ++hh) {
-          const float pw = pbuf[hh][tt];
+        for (int hh = 0; hh < GH; ++hh) acc[hh] = group_sum<LPR>(acc[hh]);
+        if (kp == LPR - 1) {
+          float* dst = &scb[(j0 + jj) * RPI + kr][0];
+          if constexpr (GH % 4 == 0) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[hh][e] = fmaf(pw, vf[e], o[hh][e]);
+            for (int hh = 0; hh < GH; hh += 4)
+              *reinterpret_cast<float4*>(dst + hh) = make_float4(acc[hh], acc[hh + 1], acc[hh + 2], acc[hh + 3]);
+          } else {
+#pragma unroll
+            for (int hh = 0; hh < GH; ++hh) dst[hh] = acc[hh];
+          }
         }
       }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  }
-  // per head: sum the RPI row groups of each 8-element part
+    };
+    // value loads: rows j * RPV + vg, VJB row steps in flight (one or two 16-byte loads each)
+    uint4 vraw[VJB][VW];
+    auto issue_v = [&](int bk, int j0) __attribute__((always_inline)) {
 #pragma unroll
-  for (int hh = 0; hh < GH; ++hh) {
+      for (int jj = 0; jj < VJB; ++jj) {
+        const int vr = rowbuf[bk][(j0 + jj) * RPV + vg];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ored[lane][e] = o[hh][e];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    float* dst = part + (((size_t)b * Hq + h0 + hh) * NS + s) * (D + 2);
-    for (int x = lane; x < D; x += 64) {
-      const int p8 = x / 8, e = x % 8;
-      float acc = 0.f;
-      for (int r2 = 0; r2 < RPI; ++r2) acc += ored[r2 * PARTS + p8][e];
-      dst[2 + x] = acc;
+        for (int x = 0; x < VW; ++x)
+          vraw[jj][x] = vr >= 0 ? *reinterpret_cast<const uint4*>(vb + (size_t)vr * rs + vp * 8 + x * EPL)
+                                : make_uint4(0, 0, 0, 0);
+      }
+    };
+    auto accum_v = [&](int j0) __attribute__((always_inline)) {
+      if constexpr (BF) {
+#pragma unroll
+        for (int jj = 0; jj < VJB; jj += 2) {   // rows ta, tb: column pairs (value of ta, value of tb)
+          const int ta = (j0 + jj) * RPV + vg, tb = ta + RPV;
+          const uint32_t wa[4] = {vraw[jj][0].x, vraw[jj][0].y, vraw[jj][0].z, vraw[jj][0].w};
+          const uint32_t wb[4] = {vraw[jj + 1][0].x, vraw[jj + 1][0].y, vraw[jj + 1][0].z, vraw[jj + 1][0].w};
+          uint32_t cp[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            cp[2 * e] = (wa[e] & 0xffffu) | (wb[e] << 16);
+            cp[2 * e + 1] = (wa[e] >> 16) | (wb[e] & 0xffff0000u);
+          }
+#pragma unroll
+          for (int hh = 0; hh < GH; ++hh) {
+            const bf16x2 pk = {(__bf16)pbuf[hh][ta], (__bf16)pbuf[hh][tb]};   // exact: already bf16 values
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              o[hh][e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, cp[e]), pk, o[hh][e], false);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < VJB; ++jj) {
+          const int tt = (j0 + jj) * RPV + vg;
+          const float vf[8] = {__uint_as_float(vraw[jj][0].x), __uint_as_float(vraw[jj][0].y),
+                               __uint_as_float(vraw[jj][0].z), __uint_as_float(vraw[jj][0].w),
+                               __uint_as_float(vraw[jj][1].x), __uint_as_float(vraw[jj][1].y),
+                               __uint_as_float(vraw[jj][1].z), __uint_as_float(vraw[jj][1].w)};
+#pragma unroll
+          for (int hh = 0; hh < GH; ++hh) {
+            const float pw = pbuf[hh][tt];       // 0 for rows past the slice (zero values too)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[hh][e] = fmaf(pw, vf[e], o[hh][e]);
+          }
+        }
+      }
+    };
+    constexpr bool PREF = NI == KB;               // a block's key loads fit in one batch: prefetch them
+    if constexpr (PREF) issue_k(0, 0);
+    for (int bk = 0; bk < nblk; ++bk) {
+      // ---- scores: key rows across lanes
+      if constexpr (PREF) {
+        score_k(0);
+      } else {
+#pragma unroll
+        for (int j0 = 0; j0 < NI; j0 += KB) {
+          issue_k(bk, j0);
+          score_k(j0);
+        }
+      }
+      // this block's first value loads and the next block's key loads go out before the softmax
+      issue_v(bk, 0);
+      if constexpr (PREF) {
+        if (bk + 1 < nblk) issue_k(bk + 1, 0);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      // ---- online softmax, one token per lane
+      const bool valid = rowbuf[bk][lane] >= 0;
+      float scl[GH];
+      if constexpr (GH % 4 == 0) {
+#pragma unroll
+        for (int hh = 0; hh < GH; hh += 4) {
+          const float4 v4 = *reinterpret_cast<const float4*>(&scb[lane][hh]);
+          scl[hh] = v4.x; scl[hh + 1] = v4.y; scl[hh + 2] = v4.z; scl[hh + 3] = v4.w;
+        }
+      } else {
+#pragma unroll
+        for (int hh = 0; hh < GH; ++hh) scl[hh] = scb[lane][hh];
+      }
+#pragma unroll
+      for (int hh = 0; hh < GH; ++hh) {
+        const float sc = valid ? (BF ? scl[hh] * scale_log2 : scl[hh]) : -INFINITY;
+        const float m_new = fmaxf(m[hh], wave_max(sc));
+        const float alpha = exp2f(m[hh] - m_new);   // m = -inf on the first block: alpha = 0
+        float p = valid ? exp2f(sc - m_new) : 0.f;
+        if constexpr (BF) p = to_f(bf16_rne(p));
+        l[hh] = l[hh] * alpha + wave_add(p);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[hh][e] *= alpha;
+        m[hh] = m_new;
+        pbuf[hh][lane] = p;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      // ---- PV
+      accum_v(0);
+#pragma unroll
+      for (int j0 = VJB; j0 < NJV; j0 += VJB) {
+        issue_v(bk, j0);
+        accum_v(j0);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     }
-    if (lane == 0) { dst[0] = m[hh]; dst[1] = l[hh]; }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // per head: sum the RPV row groups of each 8-element part
+#pragma unroll
+    for (int hh = 0; hh < GH; ++hh) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ored[lane][e] = o[hh][e];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      float* dst = part + (((size_t)b * Hq + h0 + hh) * NS + s) * (D + 2);
+      for (int x = lane; x < D; x += 64) {
+        const int p8 = x / 8, e = x % 8;
+        float acc = 0.f;
+        for (int r2 = 0; r2 < RPV; ++r2) acc += ored[r2 * PARTS + p8][e];
+        dst[2 + x] = acc;
+      }
+      if (lane == 0) { dst[0] = m[hh]; dst[1] = l[hh]; }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
   }
 }
 
@@ -548,16 +717,20 @@ hipError_t step_d(const DecodeDims& p, const DecodePtrs& s, const void* q, const
   if (err != hipSuccess) return err;
   const int R = GROUPED ? p.Hkv : p.Hq;
   hipLaunchKernelGGL((decode_route_kernel<D, GROUPED>), dim3(p.B * R), dim3(kRouteThreads), 0, stream, s.q_run, s.k_sum,
-                     s.seq_len, s.num_closed, s.chunk_start, s.status, p.Hq, p.Hkv, p.Cmax, topk, w.spans, w.nspan,
+                     s.seq_len, s.num_closed, s.chunk_start, s.status, p.Hq, p.Hkv, p.Cmax, p.L, topk, w.urow,
                      w.ntok, kept);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   // heads per attention wave: the whole group when routing per KV head (each K/V row read once for it)
   const int G = p.Hq / p.Hkv;
   const int gh = !GROUPED ? 1 : (G == 8 ? 8 : G == 4 ? 4 : G == 2 ? 2 : 1);
+  // slices per row in the grid: enough for the kept tokens of chunks of up to hi tokens (longer rows,
+  // e.g. from a prefix chunked otherwise, loop over slices with this stride)
+  const long long need = ((long long)(topk + 1) * hi + kDecodeSlice - 1) / kDecodeSlice;
+  const int NSg = (int)std::max(1LL, std::min<long long>(w.NS, need));
 #define DHSA_ATTEND(GHV)                                                                                         \
-  hipLaunchKernelGGL((decode_attend_kernel<T, D, GROUPED, GHV>), dim3(p.B * (p.Hq / GHV) * w.NS), dim3(64), 0,  \
-                     stream, (const T*)q, (const T*)s.k_cache, (const T*)s.v_cache, w.spans, w.nspan, w.ntok,     \
-                     p.Hq, p.Hkv, p.L, topk, w.NS, scale * kLog2e, w.part)
+  hipLaunchKernelGGL((decode_attend_kernel<T, D, GROUPED, GHV>), dim3(p.B * (p.Hq / GHV) * NSg), dim3(64), 0,   \
+                     stream, (const T*)q, (const T*)s.k_cache, (const T*)s.v_cache, w.urow, w.ntok, p.Hq, p.Hkv,  \
+                     p.L, NSg, w.NS, scale * kLog2e, w.part)
   if constexpr (GROUPED) {
     if (gh == 8) DHSA_ATTEND(8);
     else if (gh == 4) DHSA_ATTEND(4);

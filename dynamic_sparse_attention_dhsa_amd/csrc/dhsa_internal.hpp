@@ -71,8 +71,7 @@ struct DecodePtrs {                               // the caller's state (device)
   int32_t* status;
 };
 struct DecodeWork {                               // carved from the caller's workspace
-  int4* spans;                                    // [B * rows, topk + 1]
-  int32_t* nspan;                                 // [B * rows]
+  int32_t* urow;                                  // [B * rows, L]: cache row of each kept token, kept order
   int32_t* ntok;                                  // [B * rows]
   float* part;                                    // [B * Hq * NS, d + 2]
   int NS;                                         // slices per (sequence, q head)
