@@ -86,23 +86,54 @@ __device__ inline int wave_sum_i32(int x) {
 template <int NB>
 __device__ inline int select_tokens_and_write(const uint32_t (&ob)[kSelBatches], const int (&len)[kSelBatches],
                                               int budget, int first, int lane, int32_t* __restrict__ out) {
-  uint64_t key[NB];
+  // Keys (score bits : complemented chunk id) order the candidates by the ranking; the kept set is
+  // every key >= X for the smallest X whose kept lengths fit the budget.  The search runs over the
+  // 32 score bits first, with one 64-bit compare per candidate: (score bits << 1) | [low word all
+  // ones, i.e. chunk 0] against (threshold << 1) | 1 (empty slots are 0 and never pass); then, when
+  // several candidates tie the chosen score bits, over the chunk bits among them.  A single tied
+  // candidate is kept when it fits beside everything above it.
+  uint32_t lo[NB];
+  uint64_t k1[NB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
-    key[b] = ob[b] ? (((uint64_t)ob[b] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(first + 64 * b + lane))) : 0ull;
-  uint64_t X = 0ull;
-  for (int bit = 63; bit >= 0; --bit) {
-    const uint64_t x1 = X | ((1ull << bit) - 1ull);
+  for (int b = 0; b < NB; ++b) {
+    lo[b] = 0xFFFFFFFFu - (uint32_t)(first + 64 * b + lane);
+    k1[b] = ob[b] != 0u ? (((uint64_t)ob[b] << 1) | (lo[b] == 0xFFFFFFFFu ? 1ull : 0ull)) : 0ull;
+  }
+  uint32_t Xh = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint64_t t1 = ((uint64_t)(Xh | ((1u << bit) - 1u)) << 1) | 1ull;
     int part = 0;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) part += (key[b] != 0ull && key[b] >= x1) ? len[b] : 0;
-    if (wave_sum_i32(part) > budget) X |= 1ull << bit;
+    for (int b = 0; b < NB; ++b) part += k1[b] >= t1 ? len[b] : 0;
+    if (wave_sum_i32(part) > budget) Xh |= 1u << bit;
+  }
+  // lengths above the chosen score bits, and the candidates that tie them
+  int above = 0, tie_len = 0, ntied = 0;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const bool tie = ob[b] != 0u && ob[b] == Xh;
+    above += (ob[b] != 0u && ob[b] > Xh) ? len[b] : 0;
+    tie_len += tie ? len[b] : 0;
+    ntied += __popcll(__ballot(tie));
+  }
+  above = wave_sum_i32(above);
+  uint32_t Xl = 0u;
+  if (ntied == 1) {
+    Xl = above + wave_sum_i32(tie_len) <= budget ? 0u : 0xFFFFFFFFu;   // keep it, or not (its low word < ~0)
+  } else if (ntied > 1) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t xl = Xl | ((1u << bit) - 1u);
+      int part = 0;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) part += (ob[b] != 0u && ob[b] == Xh && lo[b] >= xl) ? len[b] : 0;
+      if (above + wave_sum_i32(part) > budget) Xl |= 1u << bit;
+    }
   }
   const uint64_t below = (1ull << lane) - 1ull;
   int pos = 0;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const bool keep = key[b] != 0ull && key[b] >= X;
+    const bool keep = ob[b] != 0u && (ob[b] > Xh || (ob[b] == Xh && lo[b] >= Xl));
     const uint64_t km = __ballot(keep);
     if (keep) out[pos + __popcll(km & below)] = first + 64 * b + lane;
     pos += __popcll(km);

@@ -212,6 +212,33 @@ def test_budget_over_register_candidates_is_refused():
         D.route_tokens(layout, plan, qs, ks)
 
 
+@pytest.mark.parametrize("grouped", [False, True])
+def test_exact_ties_break_to_lower_index_tokens(grouped):
+    """Identical integer-valued tokens with q equal to its KV head's k: a chunk's score is
+    sqrt(n_i n_j) |k|^2, so chunks of equal length tie exactly and longer ones rank first; the kept
+    lists (many exact ties at the budget boundary) must equal the oracle's entry for entry."""
+    lens = [16, 32] * 12
+    T, d = sum(lens), 128
+    w = W.make_workload([SeqSpec(T, ("explicit", lens), 0, 0)], 4, 2, d, "bf16", seed=39, name="tok_ties")
+    rng = np.random.default_rng(3)
+    proto_k = rng.integers(-2, 3, size=(1, 2, d)).astype(np.float32)
+    proto_q = np.repeat(proto_k, 2, axis=1)
+    w.q = W.f32_to_bf16_bits(np.repeat(proto_q, T, axis=0))
+    w.k = W.f32_to_bf16_bits(np.repeat(proto_k, T, axis=0))
+    budget = rng.integers(0, 400, size=w.total_chunks).astype(np.int32)
+    case = TokenCase(w, budget, grouped=grouped)
+    g = case.gpu_route()
+    assert np.array_equal(g, case.o_bidx)
+    # a row whose budget ends inside the 32-token class keeps the lowest-index 32-token chunks
+    i = w.total_chunks - 1
+    row = case.o_bidx[0, case.o_rp[i]:case.o_rp[i + 1]]
+    kept = [j for j in row.tolist() if 0 <= j < i]
+    m32 = int(budget[i]) // 32                   # the row has 11 earlier 32-token chunks
+    want = [2 * x + 1 for x in range(m32)] if m32 < 11 else None
+    if want is not None:
+        assert kept == want, (kept, want, int(budget[i]))
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("grouped", [False, True])
 def test_full_128k_token_budget(grouped):
