@@ -15,8 +15,9 @@
 // row is read once.  Per token the dot product and the two squared norms are
 // reduced across the wave in fp32; the lane of the token writes sim and the
 // cut decisions go into the word's bits by a ballot.
-// Kernel 2 (latency-bound, one wave): walks the sequences in order.  The cut
-// bitmap is staged in LDS 64 KB at a time, and a window of 64 words (4096
+// Kernel 2 (latency-bound, one workgroup): the greedy walk, split into segments
+// walked speculatively by 16 waves and stitched by one (walks from different
+// starts merge at their first common cut); a window of 64 bitmap words (4096
 // tokens, one word per lane) sits in registers, so a step that stays inside
 // the window is a mask, a ballot and a lane read, with no memory access.
 #include "dhsa_internal.hpp"
@@ -25,7 +26,6 @@ namespace dhsa {
 namespace {
 
 constexpr int kSimWaves = 4;
-constexpr int kSegWords = 8192;                   // bitmap words staged in LDS at a time (64 KB)
 constexpr int kSimTok = 16;                       // tokens per wave of the similarity kernel
 
 __device__ inline int seq_of_token(const int32_t* __restrict__ cu_seqlens, int B, int t) {
@@ -154,95 +154,133 @@ __global__ __launch_bounds__(kSimWaves * 64) void adjacent_sim_kernel(
   if (lane == 0) cut_quarters[part] = (uint16_t)bits;
 }
 
-__global__ __launch_bounds__(64) void chunk_walk_kernel(
+// One greedy step for one wave: the chunk starting at c0, in a sequence ending at e, ends at the
+// returned position.  The wave keeps a window of 64 bitmap words in registers (word win0 + lane in
+// `win`, bit i of `nz` set when word win0 + i has a cut bit) and reloads it from memory when a scan
+// leaves it.  win0 and nz are wave-uniform.
+__device__ inline int walk_step(const unsigned long long* __restrict__ cut_bits, int nwords, int lane, int c0, int e,
+                                int lo, int hi, int& win0, unsigned long long& win, unsigned long long& nz) {
+  const int a = c0 + lo;
+  const int end = min(c0 + hi, e);                // the host clamps lo, hi to T: no int overflow
+  if (a >= end) return end;
+  const int wa = a >> 6, wb = (end - 1) >> 6;
+  int w = wa;
+  while (w <= wb) {                               // scan the words [w, wb] for the first cut bit
+    if (win0 < 0 || w < win0 || w >= win0 + 64) {
+      win = (w + lane < nwords) ? cut_bits[w + lane] : 0ull;
+      nz = __ballot(win != 0ull);
+      win0 = w;
+    }
+    const int i0 = w - win0, i1 = min(wb - win0, 63);
+    unsigned long long cand = nz & (~0ull << i0) & (i1 == 63 ? ~0ull : ((2ull << i1) - 1ull));
+    while (cand) {
+      const int i = __builtin_ctzll(cand);
+      const int wi = win0 + i;
+      const unsigned lo32 = __builtin_amdgcn_readlane((unsigned)win, i);
+      const unsigned hi32 = __builtin_amdgcn_readlane((unsigned)(win >> 32), i);
+      unsigned long long v = ((unsigned long long)hi32 << 32) | lo32;
+      if (wi == wa) v &= ~0ull << (a & 63);
+      if (wi == wb && (end & 63)) v &= (1ull << (end & 63)) - 1ull;
+      if (v) return (wi << 6) + __builtin_ctzll(v);
+      cand &= cand - 1ull;
+    }
+    w = win0 + 64;                                // continue past this window
+  }
+  return end;
+}
+
+// The greedy cut is sequential, but walks from different starts merge once they reach a common cut.
+// Walk: the token line (sequences back to back; a sequence's end is always a cut) is split into
+// kWalkWaves segments, and each wave walks from its segment's first token as if a chunk started there,
+// keeping its cuts in LDS up to the first one at or past the segment's end (a list that would exceed
+// kWalkCap is dropped).  Stitch: wave 0 carries the true chain through the segments in order; where
+// the chain's position is in a segment's list, the rest of that list is the chain and is copied out,
+// otherwise it takes exact steps until it lands in the list or leaves the segment.  The result is the
+// sequential walk's, whatever the lists hold.  Last, every sequence start is looked up in cu_chunks.
+constexpr int kWalkWaves = 16;
+constexpr int kWalkCap = 2040;                    // cuts kept per segment
+
+__global__ __launch_bounds__(kWalkWaves * 64) void chunk_walk_kernel(
     const unsigned long long* __restrict__ cut_bits, const int32_t* __restrict__ cu_seqlens, int B, int ntok,
     int lo, int hi, int32_t* __restrict__ cu_chunks, int32_t* __restrict__ seq_chunk_start,
     int32_t* __restrict__ num_chunks) {
-  __shared__ unsigned long long seg[kSegWords];
-  const int lane = threadIdx.x;
+  __shared__ int32_t cuts[kWalkWaves][kWalkCap];
+  __shared__ int32_t count[kWalkWaves];           // cuts kept, or -1 for a dropped list
+  __shared__ int32_t total;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nwords = (ntok + 63) >> 6;
-  int seg0 = -1;                                  // first word staged in seg (-1: nothing yet)
-  int win0 = -1;                                  // first word of the register window
-  unsigned long long win = 0ull;                  // word win0 + lane
-  unsigned long long nz = 0ull;                   // bit i: word win0 + i has a cut bit
-  auto load_window = [&](int w0) {                // wave-uniform
-    if (seg0 < 0 || w0 < seg0 || w0 + 64 > seg0 + kSegWords) {
-      // stage the words the batch still has (at most kSegWords), 16 loads in flight per lane
-      const int n = min(kSegWords, max(nwords - w0, 64));
-      __builtin_amdgcn_wave_barrier();
-      for (int x0 = 0; x0 < n; x0 += 16 * 64) {
-        unsigned long long tmp[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int w = w0 + x0 + j * 64 + lane;
-          tmp[j] = (w < nwords) ? cut_bits[w] : 0ull;
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) seg[x0 + j * 64 + lane] = tmp[j];
+  // segments of S tokens, a whole number of bitmap words; kWalkWaves * S >= ntok
+  const int S = max(64, ((ntok + kWalkWaves - 1) / kWalkWaves + 63) / 64 * 64);
+  int win0 = -1;
+  unsigned long long win = 0ull, nz = 0ull;
+
+  // ---- walk (speculative), one segment per wave
+  {
+    const int s0 = wv * S, s1 = min(ntok, s0 + S);
+    int n = 0;
+    if (s0 < ntok) {
+      int c = s0;
+      int e = cu_seqlens[seq_of_token(cu_seqlens, B, c) + 1];
+      if (lane == 0) cuts[wv][0] = c;
+      n = 1;
+      while (c < s1) {
+        const int cut = walk_step(cut_bits, nwords, lane, c, e, lo, hi, win0, win, nz);
+        if (n < kWalkCap && lane == 0) cuts[wv][n] = cut;
+        ++n;
+        c = cut;
+        if (c == e && c < ntok) e = cu_seqlens[seq_of_token(cu_seqlens, B, c) + 1];
+        if (n > kWalkCap) break;
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      seg0 = w0;
     }
-    // words of the segment past n are past the bitmap: zero them here rather than trust stale LDS
-    win = (w0 + lane < nwords) ? seg[w0 - seg0 + lane] : 0ull;
-    nz = __ballot(win != 0ull);
-    win0 = w0;
-  };
-  auto word_at = [&](int i) {                     // word win0 + i, i wave-uniform
-    const unsigned lo32 = __builtin_amdgcn_readlane((unsigned)win, i);
-    const unsigned hi32 = __builtin_amdgcn_readlane((unsigned)(win >> 32), i);
-    return ((unsigned long long)hi32 << 32) | lo32;
-  };
-  int pos = 0;                                    // chunks written so far
-  int32_t outv = 0;                               // cu_chunks[(pos & ~63) + lane], stored 64 at a time
-  auto emit = [&](int value) {                    // cu_chunks[pos] = value
-    if (lane == (pos & 63)) outv = value;
-    if ((pos & 63) == 63) cu_chunks[(pos & ~63) + lane] = outv;
-    ++pos;
-  };
-  emit(0);
-  if (lane == 0) seq_chunk_start[0] = 0;
-  for (int b = 0; b < B; ++b) {
-    const int e = cu_seqlens[b + 1];
-    int c0 = cu_seqlens[b];
-    while (c0 < e) {
-      const int a = c0 + lo;
-      const int end = min(c0 + hi, e);            // the host clamps lo, hi to T: no int overflow
-      int cut = end;
-      if (a < end) {
-        const int wa = a >> 6, wb = (end - 1) >> 6;
-        int w = wa;
-        while (w <= wb) {                         // scan the words [w, wb] for the first cut bit
-          if (win0 < 0 || w < win0 || w >= win0 + 64) load_window(w);
-          const int i0 = w - win0, i1 = min(wb - win0, 63);
-          unsigned long long cand = nz & (~0ull << i0) & (i1 == 63 ? ~0ull : ((2ull << i1) - 1ull));
-          bool found = false;
-          while (cand) {
-            const int i = __builtin_ctzll(cand);
-            const int wi = win0 + i;
-            unsigned long long v = word_at(i);
-            if (wi == wa) v &= ~0ull << (a & 63);
-            if (wi == wb && (end & 63)) v &= (1ull << (end & 63)) - 1ull;
-            if (v) {
-              cut = (wi << 6) + __builtin_ctzll(v);
-              found = true;
-              break;
-            }
-            cand &= cand - 1ull;
-          }
-          if (found) break;
-          w = win0 + 64;                          // continue past this window
-        }
-      }
-      emit(cut);
-      c0 = cut;
-    }
-    if (lane == 0) seq_chunk_start[b + 1] = pos - 1;
+    if (lane == 0) count[wv] = n > kWalkCap ? -1 : n;
   }
-  if ((pos & 63) != 0 && lane < (pos & 63)) cu_chunks[(pos & ~63) + lane] = outv;
-  if (lane == 0) *num_chunks = pos - 1;
+  __syncthreads();
+
+  // ---- stitch, one wave
+  if (wv == 0) {
+    win0 = -1;
+    if (lane == 0) cu_chunks[0] = 0;
+    int c = 0, pos = 0;
+    while (c < ntok) {
+      const int k = c / S;
+      const int n = count[k];
+      int m = -1;
+      if (n > 0) {                                // the list is strictly increasing: binary search for c
+        int l = 0, r = n - 1;
+        while (l < r) {
+          const int mid = (l + r) >> 1;
+          if (cuts[k][mid] < c) l = mid + 1; else r = mid;
+        }
+        if (cuts[k][l] == c) m = l;
+      }
+      if (m >= 0) {                               // the chain from c is this list's: copy the rest out
+        const int cnt = n - 1 - m;
+        for (int x = lane; x < cnt; x += 64) cu_chunks[pos + 1 + x] = cuts[k][m + 1 + x];
+        pos += cnt;
+        c = cuts[k][n - 1];                       // at or past the segment's end, or the last token
+      } else {                                    // one exact step
+        const int e = cu_seqlens[seq_of_token(cu_seqlens, B, c) + 1];
+        const int cut = walk_step(cut_bits, nwords, lane, c, e, lo, hi, win0, win, nz);
+        if (lane == 0) cu_chunks[pos + 1] = cut;
+        ++pos;
+        c = cut;
+      }
+    }
+    if (lane == 0) { total = pos; *num_chunks = pos; }
+  }
+  __syncthreads();
+
+  // ---- sequence starts: each is a cut (or 0), found in cu_chunks[0 .. total]
+  const int nc = total;
+  for (int b = tid; b <= B; b += kWalkWaves * 64) {
+    const int v = cu_seqlens[b];
+    int l = 0, r = nc;
+    while (l < r) {
+      const int mid = (l + r) >> 1;
+      if (cu_chunks[mid] < v) l = mid + 1; else r = mid;
+    }
+    seq_chunk_start[b] = l;
+  }
 }
 
 }  // namespace
@@ -274,7 +312,7 @@ hipError_t launch_adjacent_similarity(int B, int ntok, int W, int dtype, const i
 
 hipError_t launch_chunk_walk(int B, int ntok, const int32_t* cu_seqlens, const uint64_t* cut_bits, int lo, int hi,
                              int32_t* cu_chunks, int32_t* seq_chunk_start, int32_t* num_chunks, hipStream_t stream) {
-  hipLaunchKernelGGL(chunk_walk_kernel, dim3(1), dim3(64), 0, stream, (const unsigned long long*)cut_bits,
+  hipLaunchKernelGGL(chunk_walk_kernel, dim3(1), dim3(kWalkWaves * 64), 0, stream, (const unsigned long long*)cut_bits,
                      cu_seqlens, B, ntok, lo, hi, cu_chunks, seq_chunk_start, num_chunks);
   return hipGetLastError();
 }
