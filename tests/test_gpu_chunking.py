@@ -114,3 +114,23 @@ def test_walk_restages_the_bitmap():
     w = W.make_workload([SeqSpec(350000, ("uniform", 32, 400), 0, 0), SeqSpec(250000, ("uniform", 16, 100), 0, 0)],
                         1, 1, 64, "bf16", seed=38, name="long")
     _check(w, 8, 300, 0.5)
+
+
+def test_walk_segments_that_never_merge_and_dropped_lists():
+    """The walk runs its segments speculatively from their first tokens and stitches them; the result
+    must be the sequential walk's also where the speculative walks never meet the true chain and where
+    a segment holds more cuts than its list keeps."""
+    # constant rows: no cut bits, chunks of hi = 100; the 16 segments start at multiples of 320, most of
+    # them between two true cuts, and walks from there stay offset (every chunk is hi long)
+    T = 5000
+    w = W.make_workload([SeqSpec(T, ("fixed", T), 0, 0)], 1, 1, 64, "bf16", seed=41, name="nomerge")
+    row = W.f32_to_bf16_bits(np.linspace(-1, 1, 64, dtype=np.float32).reshape(1, 1, 64))
+    w.k = np.repeat(row, T, axis=0)
+    cu, _, _ = _check(w, 10, 100, 0.99)
+    assert cu.tolist() == list(range(0, T, 100)) + [T]
+    # one-token chunks over 40000 tokens: 2500 cuts per segment, more than a list keeps
+    T = 40000
+    w = W.make_workload([SeqSpec(T - 1, ("fixed", 64), 0, 0), SeqSpec(1, ("fixed", 1), 0, 0)], 1, 1, 64, "bf16",
+                        seed=42, name="dropped")
+    cu, scs, _ = _check(w, 1, 1, 0.5)
+    assert cu.tolist() == list(range(T + 1)) and scs.tolist() == [0, T - 1, T]
