@@ -280,7 +280,20 @@ def cpu_baseline(w, topk, budget_s: float, grouped: bool = False):
                        f"on {n_rows} random (head, chunk) rows = {done_tok} query-token-heads of "
                        f"{w.total_tokens * w.num_q_heads} ({t_att:.1f} s), attention time extrapolated per "
                        f"query-token-head; fp64 numpy"),
-            "seconds_est_full_step": t_full}
+            "seconds_est_full_step": t_full, "cpu_model": _cpu_model(),
+            "stage_seconds": {"summaries": t_sum, "routing": t_route, "attention_sample": t_att}}
+
+
+def _cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo; empty where that is not readable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
 
 
 def main() -> int:
