@@ -588,12 +588,14 @@ __global__ __launch_bounds__(64) void decode_attend_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------- combine
-// Per (sequence, q head): the slices' weights exp2(m_s - M) from one pass over (m_s, l_s) with wave
-// reductions (64 slices at a time), then out = sum_s w_s o_s / sum_s w_s l_s, eight slices' loads in flight.
+// Per (sequence, q head): the slices' (m_s, l_s), one slice per lane, their weights exp2(m_s - M) by
+// wave reductions, then out = sum_s w_s o_s / sum_s w_s l_s with the columns of 64 / XPL slices in
+// flight at once.
 template <typename T, int D, bool GROUPED>
 __global__ __launch_bounds__(64) void decode_combine_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ ntok, const int32_t* __restrict__ status,
     int Hq, int Hkv, int NS, T* __restrict__ out) {
+  constexpr int XPL = (D + 63) / 64;              // output columns per lane
   __shared__ float wgt[kDecodeMaxSlices];
   const int bh = blockIdx.x, lane = threadIdx.x;
   const int b = bh / Hq, h = bh % Hq;
@@ -607,31 +609,54 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
   }
   const int nsl = (n + kDecodeSlice - 1) / kDecodeSlice;   // <= NS <= kDecodeMaxSlices
   const float* pp = part + (size_t)bh * NS * (D + 2);
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < nsl; s0 += 64) {
-    const int s = s0 + lane;
-    M = fmaxf(M, wave_max(s < nsl ? pp[(size_t)s * (D + 2)] : -INFINITY));
+  // slice lane in registers; slices past 64 (rows over 64 slices) are read again for their weights
+  const float m0 = lane < nsl ? pp[(size_t)lane * (D + 2)] : -INFINITY;
+  const float l0 = lane < nsl ? pp[(size_t)lane * (D + 2) + 1] : 0.f;
+  float M = m0;
+  for (int sl = 64 + lane; sl < nsl; sl += 64) M = fmaxf(M, pp[(size_t)sl * (D + 2)]);
+  M = wave_max(M);
+  float Lpart = 0.f;
+  if (lane < nsl) {
+    const float w = exp2f(m0 - M);
+    wgt[lane] = w;
+    Lpart = w * l0;
   }
-  float Lsum = 0.f;
-  for (int s0 = 0; s0 < nsl; s0 += 64) {
-    const int s = s0 + lane;
-    float w = 0.f, l = 0.f;
-    if (s < nsl) {
-      w = exp2f(pp[(size_t)s * (D + 2)] - M);
-      l = pp[(size_t)s * (D + 2) + 1];
-      wgt[s] = w;
-    }
-    Lsum += wave_add(w * l);
+  for (int sl = 64 + lane; sl < nsl; sl += 64) {
+    const float w = exp2f(pp[(size_t)sl * (D + 2)] - M);
+    wgt[sl] = w;
+    Lpart += w * pp[(size_t)sl * (D + 2) + 1];
   }
+  const float inv = 1.0f / wave_add(Lpart);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  const float inv = 1.0f / Lsum;
-  for (int x = lane; x < D; x += 64) {
-    float acc = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < nsl; ++s) acc = fmaf(wgt[s], pp[(size_t)s * (D + 2) + 2 + x], acc);
-    from_f(acc * inv, op[x]);
+  float acc[XPL];
+#pragma unroll
+  for (int i = 0; i < XPL; ++i) acc[i] = 0.f;
+  for (int s0 = 0; s0 < nsl; s0 += 64) {
+    const int cnt = min(64, nsl - s0);
+    float v[XPL][64 / XPL];
+    // columns x = lane + 64 i of slices s0 .. s0 + cnt - 1, all loads of a batch issued before use
+    for (int s1 = 0; s1 < cnt; s1 += 64 / XPL) {
+#pragma unroll
+      for (int j = 0; j < 64 / XPL; ++j)
+#pragma unroll
+        for (int i = 0; i < XPL; ++i) {
+          const int x = lane + 64 * i;
+          const int sl = s0 + s1 + j;
+          v[i][j] = (x < D && s1 + j < cnt) ? pp[(size_t)sl * (D + 2) + 2 + x] : 0.f;
+        }
+#pragma unroll
+      for (int j = 0; j < 64 / XPL; ++j)
+#pragma unroll
+        for (int i = 0; i < XPL; ++i)
+          if (s1 + j < cnt) acc[i] = fmaf(wgt[s0 + s1 + j], v[i][j], acc[i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < XPL; ++i) {
+    const int x = lane + 64 * i;
+    if (x < D) from_f(acc[i] * inv, op[x]);
   }
 }
 

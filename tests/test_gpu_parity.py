@@ -338,3 +338,19 @@ def test_full_config_grouped_sampled():
     print(f"[cfg3 grouped] kept sets: {eq} equal rows, {tol} tolerated swaps", flush=True)
     heads, chunks = _sample_rows(case)
     check_end_to_end(case, heads, chunks)
+
+
+@pytest.mark.slow
+def test_maximum_chunks_per_sequence():
+    """8192 chunks in one sequence (the supported maximum): rows past 1024 candidates take the general
+    sorting kernel, the prefill's chunk bitmaps are at their largest; every row's kept set against
+    the oracle, attention on sampled rows, among them the last chunk's (8191 candidates)."""
+    n, C = 4, 8192
+    w = small([SeqSpec(n * C, ("fixed", n), 0, 0)], 2, 1, 64, "bf16", 43, "max_chunks")
+    assert w.total_chunks == C
+    i_loc = np.arange(C)
+    tk = np.where(i_loc % 5 == 0, 100, np.where(i_loc % 5 == 1, 1500, 7)).astype(np.int32)
+    case = Case(w, topk=tk)
+    _, eq, tol = check_routing(case)
+    print(f"[max chunks] kept sets: {eq} equal rows, {tol} tolerated swaps", flush=True)
+    check_attention(case, heads=[0, 1], chunks=[0, 1, 1023, 1024, 1025, 4000, 8190, 8191])
