@@ -2,6 +2,7 @@
 // and dispatch to the gfx950 kernels.  Nothing here allocates device memory or
 // synchronises; every failure is reported before any kernel is enqueued.
 #include <math.h>
+#include <stdint.h>
 
 #include <algorithm>
 #include <vector>
@@ -79,6 +80,12 @@ dhsa_status check_row_ptr(const dhsa_layout* L, const int32_t* h_row_ptr, int64_
 
 dhsa_status launched(hipError_t e) { return e == hipSuccess ? DHSA_OK : DHSA_ERR_LAUNCH; }
 
+// Tensors the kernels read or write with 16-byte vector or buffer accesses: base pointers 16-byte
+// aligned (NULL passes here; the null checks come first).
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+template <typename... P>
+bool all_aligned16(const P*... p) { return (aligned16(p) && ...); }
+
 // Decode state: shapes, capacities and pointers (host-side view only).
 dhsa_status check_decode_state(const dhsa_decode_state* st, dhsa::DecodeDims* dims, dhsa::DecodePtrs* ptrs) {
   if (st == nullptr) return DHSA_ERR_NULL_ARG;
@@ -101,6 +108,7 @@ dhsa_status check_decode_state(const dhsa_decode_state* st, dhsa::DecodeDims* di
       st->chunk_start == nullptr || st->k_sum == nullptr || st->q_run == nullptr || st->k_run == nullptr ||
       st->status == nullptr)
     return DHSA_ERR_NULL_ARG;
+  if (!all_aligned16(st->k_cache, st->v_cache, st->k_sum, st->q_run, st->k_run)) return DHSA_ERR_BAD_SHAPE;
   *dims = dhsa::DecodeDims{st->num_seqs, st->num_q_heads, st->num_kv_heads, st->head_dim, st->dtype,
                            st->max_tokens, st->max_chunks};
   *ptrs = dhsa::DecodePtrs{st->k_cache, st->v_cache, st->seq_len, st->num_closed, st->chunk_start,
@@ -260,6 +268,7 @@ dhsa_status dhsa_chunk_summarize(const dhsa_layout* layout, const void* q, const
   if (st != DHSA_OK) return st;
   if (p.C == 0) return DHSA_OK;
   if (q == nullptr || k == nullptr || q_sum == nullptr || k_sum == nullptr) return DHSA_ERR_NULL_ARG;
+  if (!all_aligned16(q, k, q_sum, k_sum)) return DHSA_ERR_BAD_SHAPE;
   return launched(dhsa::launch_summarize(p, q, k, q_sum, k_sum, (hipStream_t)stream));
 }
 
@@ -275,6 +284,7 @@ static dhsa_status route_common(const dhsa_layout* layout, const float* q_sum, c
   if (p.C == 0) return DHSA_OK;
   if (q_sum == nullptr || k_sum == nullptr || row_ptr == nullptr || block_idx == nullptr)
     return DHSA_ERR_NULL_ARG;
+  if (!all_aligned16(q_sum, k_sum)) return DHSA_ERR_BAD_SHAPE;
   return launched(dhsa::launch_route(p, q_sum, k_sum, row_ptr, nnz, block_idx, wide, grouped,
                                      (hipStream_t)stream));
 }
@@ -308,6 +318,7 @@ dhsa_status dhsa_route_tokens(const dhsa_layout* layout, const float* q_sum, con
   if (p.C == 0) return DHSA_OK;
   if (q_sum == nullptr || k_sum == nullptr || token_budget == nullptr || row_ptr == nullptr || block_idx == nullptr)
     return DHSA_ERR_NULL_ARG;
+  if (!all_aligned16(q_sum, k_sum)) return DHSA_ERR_BAD_SHAPE;
   return launched(dhsa::launch_route_tokens(p, q_sum, k_sum, token_budget, row_ptr, nnz, block_idx, grouped != 0,
                                             (hipStream_t)stream));
 }
@@ -327,6 +338,7 @@ dhsa_status dhsa_sparse_prefill(const dhsa_layout* layout, const void* q, const 
   if (q == nullptr || k == nullptr || v == nullptr || row_ptr == nullptr || block_idx == nullptr ||
       out == nullptr)
     return DHSA_ERR_NULL_ARG;
+  if (!all_aligned16(q, k, v, out)) return DHSA_ERR_BAD_SHAPE;
   hipStream_t s = (hipStream_t)stream;
   // the bf16 kernel addresses one KV head's rows with 32-bit buffer offsets
   if (p.dtype == DHSA_BF16 && (int64_t)p.T * p.Hkv * p.d * 2 > (int64_t)INT32_MAX) return DHSA_ERR_UNSUPPORTED;
@@ -350,6 +362,7 @@ dhsa_status dhsa_adjacent_similarity(int32_t num_seqs, int32_t total_tokens, int
   if (!isfinite(tau)) return DHSA_ERR_BAD_SHAPE;
   if (total_tokens == 0) return DHSA_OK;
   if (k == nullptr || sim == nullptr || cut_bits == nullptr) return DHSA_ERR_NULL_ARG;
+  if (!all_aligned16(k)) return DHSA_ERR_BAD_SHAPE;
   return launched(dhsa::launch_adjacent_similarity(num_seqs, total_tokens, W, dtype, cu_seqlens, k, tau, sim,
                                                    cut_bits, (hipStream_t)stream));
 }
@@ -393,6 +406,7 @@ dhsa_status dhsa_decode_load_prefix(const dhsa_decode_state* state, const dhsa_l
     if (prefix->h_seq_chunk_start[b + 1] - prefix->h_seq_chunk_start[b] > p.Cmax + 1) return DHSA_ERR_BAD_SHAPE;
   }
   if (pl.T > 0 && (q == nullptr || k == nullptr || v == nullptr)) return DHSA_ERR_NULL_ARG;
+  if (!all_aligned16(q, k, v)) return DHSA_ERR_BAD_SHAPE;
   return launched(dhsa::launch_decode_load(p, s, pl, q, k, v, (hipStream_t)stream));
 }
 
@@ -408,6 +422,7 @@ dhsa_status dhsa_decode_step(const dhsa_decode_state* state, const void* q, cons
   if (topk < 0 || topk >= dhsa::kDecodeMaxChunks) return DHSA_ERR_BAD_BUDGET;
   if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return DHSA_ERR_BAD_SHAPE;
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || workspace == nullptr) return DHSA_ERR_NULL_ARG;
+  if (!all_aligned16(q, k, v, out)) return DHSA_ERR_BAD_SHAPE;
   if (((uintptr_t)workspace & 255) != 0) return DHSA_ERR_BAD_SHAPE;
   dhsa::DecodeWork w;
   if (decode_workspace(p, topk, grouped != 0, &w, workspace) > workspace_bytes) return DHSA_ERR_BAD_SHAPE;

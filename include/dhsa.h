@@ -20,7 +20,7 @@
  *      q   [T, Hq,  d]   k, v [T, Hkv, d]   out [T, Hq, d]   (row-major, contiguous)
  *      q_sum [C, Hq, d], k_sum [C, Hkv, d]  float32
  *    q/k/v/out are float32 (DHSA_F32) or bfloat16 (DHSA_BF16).  Base pointers
- *    must be 16-byte aligned.
+ *    of tensors must be 16-byte aligned (checked: DHSA_ERR_BAD_SHAPE otherwise).
  *  - GQA: query head h reads KV head h / (Hq / Hkv); Hq % Hkv == 0.
  *  - Chunk ids are global (0..C-1); the chunks of sequence b are
  *    seq_chunk_start[b] .. seq_chunk_start[b+1]-1 and tile its tokens exactly.

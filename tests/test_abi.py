@@ -317,3 +317,28 @@ def test_decode_calls_reject_before_launch():
     assert lib.dhsa_decode_load_prefix(ctypes.byref(state(num_seqs=3)), m.ref(), vp(FAKE), vp(FAKE), vp(FAKE), None) == SHAPE
     assert lib.dhsa_decode_load_prefix(ctypes.byref(state(max_tokens=8)), m.ref(), vp(FAKE), vp(FAKE), vp(FAKE), None) == SHAPE
     assert lib.dhsa_decode_load_prefix(ctypes.byref(state(max_chunks=0)), m.ref(), vp(FAKE), vp(FAKE), vp(FAKE), None) == SHAPE
+
+
+def test_misaligned_tensors_are_refused_before_launch():
+    """Base pointers of tensors read or written with 16-byte accesses must be 16-byte aligned."""
+    lib = Bd.load_library()
+    vp = ctypes.c_void_p
+    m = Mirror(*GOOD)
+    rp = np.array([0, 1, 2, 3, 5], np.int32)
+    assert lib.dhsa_chunk_summarize(m.ref(), FAKE + 8, FAKE, FAKE, FAKE, None) == SHAPE
+    assert lib.dhsa_chunk_summarize(m.ref(), FAKE, FAKE, FAKE + 4, FAKE, None) == SHAPE
+    assert lib.dhsa_route(m.ref(), FAKE + 4, FAKE, FAKE, rp.ctypes.data, 5, FAKE, None) == SHAPE
+    assert lib.dhsa_sparse_prefill(m.ref(), FAKE, FAKE, FAKE + 2, FAKE, rp.ctypes.data, 5, FAKE, 0.1, FAKE, None,
+                                   None) == SHAPE
+    assert lib.dhsa_sparse_prefill(m.ref(), FAKE, FAKE, FAKE, FAKE, rp.ctypes.data, 5, FAKE, 0.1, FAKE + 8, None,
+                                   None) == SHAPE
+    cs = np.array([0, 10, 17], np.int32)
+    assert lib.dhsa_adjacent_similarity(2, 17, 2, 128, 1, FAKE, cs.ctypes.data, FAKE + 2, 0.5, FAKE, FAKE,
+                                        None) == SHAPE
+    st = Bd.DecodeStateStruct(2, 8, 2, 128, 1, 4096, 256, *([FAKE] * 9))
+    assert lib.dhsa_decode_workspace_bytes(ctypes.byref(st), 4, 0) > 0
+    st.k_cache = FAKE + 8
+    assert lib.dhsa_decode_workspace_bytes(ctypes.byref(st), 4, 0) == 0
+    st.k_cache = FAKE
+    assert lib.dhsa_decode_step(ctypes.byref(st), vp(FAKE + 2), vp(FAKE), vp(FAKE), 8, 64, 0.5, 4, 0, 0.1, vp(FAKE),
+                                None, vp(FAKE * 256), 1 << 30, None) == SHAPE
