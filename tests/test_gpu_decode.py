@@ -127,6 +127,9 @@ CASES = {
     "no_budget": ([SeqSpec(300, ("uniform", 24, 80), 0, 0)], 4, 2, 128, "bf16", 56, 250, 16, 100, 0.5, 0),
     "from_empty": ([SeqSpec(160, ("uniform", 16, 40), 0, 0)], 4, 2, 64, "bf16", 57, 0, 8, 48, 0.5, 2),
     "long_slices": ([SeqSpec(5000, ("uniform", 400, 1000), 0, 0)], 4, 1, 128, "bf16", 58, 4970, 64, 1024, 0.5, 3),
+    # group sizes outside {1, 2, 4, 8} (one q head per attention wave when routing per KV head) and 8
+    "bf16_d128_g3": ([SeqSpec(600, ("uniform", 24, 100), 0, 0)], 6, 2, 128, "bf16", 60, 480, 16, 120, 0.5, 3),
+    "bf16_d128_g8": ([SeqSpec(600, ("uniform", 24, 100), 0, 0)], 16, 2, 128, "bf16", 61, 480, 16, 120, 0.5, 3),
 }
 
 
@@ -153,3 +156,47 @@ def test_full_cache_stops_the_sequence():
 def test_decode_32k_context():
     seqs = [SeqSpec(32768 + 24, ("uniform", 64, 512), 0, 0)]
     _check(seqs, 32, 8, 128, "bf16", 60, 32768, 32, 1024, 0.5, 32, grouped=False)
+
+
+def test_rows_longer_than_the_slice_grid():
+    """The attention grid covers (topk + 1) * hi kept tokens per row; a prefix chunked with longer chunks
+    keeps more, and the waves then loop over slices.  Each step's output must equal exact attention
+    over the kept closed chunks the step reports plus the open chunk, from the state's own chunk table
+    (self-consistency: the decode oracle would chunk the prefix by the step's rule instead)."""
+    Hq, Hkv, d, dt = 4, 2, 64, "bf16"
+    T_seq, P = 1400, 1380
+    w = W.make_workload([SeqSpec(T_seq, ("uniform", 300, 500), 0, 0)], Hq, Hkv, d, dt, seed=62, name="longrows")
+    qf, kf, vf = w.q_f32(), w.k_f32(), w.v_f32()
+    tdt = torch.bfloat16
+    scale = 1.0 / np.sqrt(d)
+    kp = _dev(w.k[:P], dt)
+    cu_p = np.array([0, P], np.int32)
+    cc, scs = D.online_chunks(kp, cu_p, 64, 512, 0.5)
+    assert np.diff(cc).max() > 256
+    state = D.DecodeState(1, Hq, Hkv, d, tdt, T_seq, 64)
+    state.load_prefix(D.Layout(cu_p, cc, scs, Hq, Hkv, d, tdt), _dev(w.q[:P], dt), kp, _dev(w.v[:P], dt))
+    lo, hi, tau, topk = 8, 16, 0.5, 6
+    kept_buf = torch.empty((1, Hq, topk), dtype=torch.int32, device="cuda")
+    G = Hq // Hkv
+    longest = 0
+    for t in range(P, P + 12):
+        o = state.step(_dev(w.q[t:t + 1], dt), _dev(w.k[t:t + 1], dt), _dev(w.v[t:t + 1], dt), lo, hi, tau, topk,
+                       False, scale, kept=kept_buf)
+        out = o.float().cpu().numpy()[0]
+        kept = kept_buf.cpu().numpy()[0]
+        nc = int(state.num_closed[0].item())
+        starts = state.chunk_start[0, :nc + 1].cpu().numpy().tolist()
+        for h in range(Hq):
+            rows = []
+            for j in kept[h].tolist():
+                if j >= 0:
+                    rows += list(range(starts[j], starts[j + 1]))
+            rows += list(range(starts[nc], t + 1))
+            longest = max(longest, len(rows))
+            kk = kf[rows, h // G].astype(np.float64)
+            z = scale * (kk @ qf[t, h].astype(np.float64))
+            p = np.exp(z - z.max())
+            ref = (p / p.sum()) @ vf[rows, h // G].astype(np.float64)
+            err = np.abs(out[h] - ref).max()
+            assert err <= OUT_ATOL[dt], (t, h, err)
+    assert longest > (topk + 1) * hi and longest > 2 * 256     # several slices for one wave

@@ -169,6 +169,11 @@ SMALL = {
     "f32_d128_g2": lambda: small([SeqSpec(400, ("uniform", 10, 90), 3, 1), SeqSpec(250, ("uniform", 40, 60), 1, 0)],
                                  4, 2, 128, "f32", 17, "f32_d128"),
     "f32_d32": lambda: small([SeqSpec(300, ("uniform", 5, 50), 2, 1)], 2, 1, 32, "f32", 18, "f32_d32"),
+    # group sizes that are not a power of two (one head per workgroup slot) and larger than four
+    "bf16_d128_g3": lambda: small([SeqSpec(800, ("uniform", 20, 130), 4, 2), SeqSpec(200, ("uniform", 8, 40), 2, 0)],
+                                  6, 2, 128, "bf16", 19, "g3"),
+    "bf16_d128_g16": lambda: small([SeqSpec(900, ("uniform", 24, 200), 5, 2)], 32, 2, 128, "bf16", 20, "g16",
+                                   topics_per_head=True),
 }
 
 
@@ -200,7 +205,7 @@ def test_small_end_to_end(small_case):
 # routing once per KV head: the group's row, checked against the oracle's grouped routing, and the
 # whole path end to end with it
 GROUPED = ("bf16_d128_g4_ragged", "bf16_d128_g8_long_chunks", "bf16_d256_g2", "bf16_d64_g1", "bf16_divergent_heads",
-           "f32_d128_g2")
+           "f32_d128_g2", "bf16_d128_g3", "bf16_d128_g16")
 
 
 @pytest.mark.parametrize("name", GROUPED)
