@@ -118,17 +118,20 @@ dhsa_status check_decode_state(const dhsa_decode_state* st, dhsa::DecodeDims* di
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace layout of a decode step: the kept tokens' cache rows, token counts, split-K partial states.
+// Workspace layout of a decode step: the kept tokens' cache rows, token counts, split-K partial states,
+// each sequence's pending append record.
 size_t decode_workspace(const dhsa::DecodeDims& p, int topk, bool grouped, dhsa::DecodeWork* w, void* base) {
   const size_t rows = (size_t)p.B * (grouped ? p.Hkv : p.Hq);
   const int NS = (p.L + dhsa::kDecodeSlice - 1) / dhsa::kDecodeSlice;
   const size_t o_urow = 0;
   const size_t o_ntok = align256(o_urow + rows * (size_t)p.L * sizeof(int32_t));
   const size_t o_part = align256(o_ntok + rows * sizeof(int32_t));
-  const size_t total = align256(o_part + (size_t)p.B * p.Hq * NS * (p.d + 2) * sizeof(float));
+  const size_t o_pend = align256(o_part + (size_t)p.B * p.Hq * NS * (p.d + 2) * sizeof(float));
+  const size_t total = align256(o_pend + (size_t)p.B * 4 * sizeof(int32_t));
   if (w != nullptr) {
     char* c = (char*)base;
-    *w = dhsa::DecodeWork{(int32_t*)(c + o_urow), (int32_t*)(c + o_ntok), (float*)(c + o_part), NS};
+    *w = dhsa::DecodeWork{(int32_t*)(c + o_urow), (int32_t*)(c + o_ntok), (float*)(c + o_part),
+                          (int32_t*)(c + o_pend), NS};
   }
   return total;
 }

@@ -36,7 +36,6 @@ namespace {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kAppendThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ inline float to_f(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
@@ -75,80 +74,6 @@ __device__ inline float wave_max(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
-// ---------------------------------------------------------------------------------------------- append
-template <typename T>
-__global__ __launch_bounds__(kAppendThreads) void decode_append_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ k_cache,
-    T* __restrict__ v_cache, int32_t* __restrict__ seq_len, int32_t* __restrict__ num_closed,
-    int32_t* __restrict__ chunk_start, float* __restrict__ k_sum, float* __restrict__ q_run,
-    float* __restrict__ k_run, int32_t* __restrict__ status, int Hq, int Hkv, int d, int L, int Cmax, int lo,
-    int hi, float tau) {
-  __shared__ float red[3][kAppendThreads / 64];
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int Wk = Hkv * d, Wq = Hq * d;
-  if (status[b] != 0) return;                     // block-uniform: a stopped sequence stays stopped
-  const int t = seq_len[b];
-  const int nc = num_closed[b];
-  const int c0 = chunk_start[(size_t)b * (Cmax + 1) + nc];
-  if (t >= L) {                                   // the cache is full
-    if (tid == 0) status[b] = 1;
-    return;
-  }
-  const T* kn = k + (size_t)b * Wk;
-  const T* vn = v + (size_t)b * Wk;
-  const T* qn = q + (size_t)b * Wq;
-  T* kc = k_cache + (size_t)b * L * Wk;
-  T* vc = v_cache + (size_t)b * L * Wk;
-  // cosine with the previous key row
-  float dot = 0.f, na = 0.f, nb = 0.f;
-  if (t > 0) {
-    for (int x = tid; x < Wk; x += kAppendThreads) {
-      const float a = to_f(kc[(size_t)(t - 1) * Wk + x]), c = to_f(kn[x]);
-      dot = fmaf(a, c, dot);
-      na = fmaf(a, a, na);
-      nb = fmaf(c, c, nb);
-    }
-  }
-  dot = wave_add(dot);
-  na = wave_add(na);
-  nb = wave_add(nb);
-  if (lane == 0) { red[0][wave] = dot; red[1][wave] = na; red[2][wave] = nb; }
-  __syncthreads();
-  dot = na = nb = 0.f;
-#pragma unroll
-  for (int w = 0; w < kAppendThreads / 64; ++w) { dot += red[0][w]; na += red[1][w]; nb += red[2][w]; }
-  const float s = (t > 0 && na > 0.f && nb > 0.f) ? dot / (sqrtf(na) * sqrtf(nb)) : 1.0f;
-  const int n_open = t - c0;
-  const bool cut = t > 0 && ((n_open >= lo && s < tau) || n_open >= hi);
-  if (cut && nc + 1 > Cmax) {                     // no room for another closed chunk
-    if (tid == 0) status[b] = 2;
-    return;
-  }
-  float* kr = k_run + (size_t)b * Wk;
-  float* qr = q_run + (size_t)b * Wq;
-  if (cut) {
-    const float inv = 1.0f / sqrtf((float)n_open);
-    float* ks = k_sum + ((size_t)b * Cmax + nc) * Wk;
-    for (int x = tid; x < Wk; x += kAppendThreads) {
-      ks[x] = kr[x] * inv;
-      kr[x] = to_f(kn[x]);
-    }
-    for (int x = tid; x < Wq; x += kAppendThreads) qr[x] = to_f(qn[x]);
-    if (tid == 0) {
-      num_closed[b] = nc + 1;
-      chunk_start[(size_t)b * (Cmax + 1) + nc + 1] = t;
-    }
-  } else {
-    for (int x = tid; x < Wk; x += kAppendThreads) kr[x] += to_f(kn[x]);
-    for (int x = tid; x < Wq; x += kAppendThreads) qr[x] += to_f(qn[x]);
-  }
-  for (int x = tid; x < Wk; x += kAppendThreads) {
-    kc[(size_t)t * Wk + x] = kn[x];
-    vc[(size_t)t * Wk + x] = vn[x];
-  }
-  if (tid == 0) seq_len[b] = t + 1;
-}
-
 // ---------------------------------------------------------------------------------------------- route
 // Sum over the LS consecutive lanes that read one summary row (LS in {16, 32, 64}) on the DPP paths;
 // lane LS - 1 of each group holds the sum.
@@ -164,46 +89,116 @@ __device__ inline float row_sum(float x) {
 }
 
 // One workgroup (kRouteThreads) per (sequence, row); a row is a q head, or a KV head when routing per
-// KV head.  Each wave scores a contiguous range of closed chunks into LDS, reading the key summaries
-// across lanes; wave 0 then holds the scores in registers, selects the top-k and lays out the row's
-// kept spans (closed chunks ascending, then the open chunk) with their token offsets; every wave then
-// writes the spans' cache rows into the row array, and wave 0 the row's total kept tokens.
+// KV head.  The workgroup first takes the token's append decision itself (the cosine of the new key
+// row with the previous one over every KV head, then the chunking rule), so every workgroup of a
+// sequence reads the state as it was before the token and none waits for another: the owner of KV
+// head g (the row itself when routing per KV head, else the group's first q head) writes the token's
+// cache row and, at a cut, the closed chunk's key summary for head g; every workgroup keeps that
+// summary in LDS and scores it from there; the sequence's counters and running sums are committed by
+// the combine launch (from the pending record the row-0 workgroup leaves).  Then each wave scores a
+// contiguous range of closed chunks into LDS, reading the key summaries across lanes; wave 0 holds
+// the scores in registers, selects the top-k and lays out the row's kept spans (closed chunks
+// ascending, then the open chunk) with their token offsets; every wave writes the spans' cache rows
+// into the row array, and wave 0 the row's total kept tokens.
 constexpr int kRouteThreads = 1024;
 
-template <int D, bool GROUPED>
+template <typename T, int D, bool GROUPED>
 __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(
-    const float* __restrict__ q_run, const float* __restrict__ k_sum, const int32_t* __restrict__ seq_len,
-    const int32_t* __restrict__ num_closed, const int32_t* __restrict__ chunk_start,
-    const int32_t* __restrict__ status, int Hq, int Hkv, int Cmax, int L, int topk, int32_t* __restrict__ urow,
-    int32_t* __restrict__ ntok, int32_t* __restrict__ kept_out) {
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ k_cache,
+    T* __restrict__ v_cache, float* __restrict__ k_sum, const float* __restrict__ q_run,
+    const float* __restrict__ k_run, const int32_t* __restrict__ seq_len, const int32_t* __restrict__ num_closed,
+    const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ status, int Hq, int Hkv, int Cmax, int L,
+    int topk, int lo, int hi, float tau, int32_t* __restrict__ urow, int32_t* __restrict__ ntok,
+    int32_t* __restrict__ kept_out, int4* __restrict__ pend) {
   __shared__ __attribute__((aligned(16))) float qv[D];
+  __shared__ __attribute__((aligned(16))) float ksn[D];   // key summary of the chunk this token closes
+  __shared__ float red[3][kRouteThreads / 64];
   __shared__ float scores[sel::kSelCand];
   __shared__ int32_t kl[sel::kSelCand];
   __shared__ int3 span_lds[sel::kSelCand + 1];
   __shared__ int32_t cs_l[sel::kSelCand + 1];    // chunk starts of the sequence, closed chunks then c0
   const int R = GROUPED ? Hkv : Hq;
-  const int b = blockIdx.x / R, r = blockIdx.x % R, tid = threadIdx.x, lane = tid & 63;
+  const int b = blockIdx.x / R, r = blockIdx.x % R, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int G = Hq / Hkv;
   const int g = GROUPED ? r : r / G;
+  const bool owner = GROUPED || r % G == 0;       // writes KV head g's cache row and closed summary
+  const int Wk = Hkv * D, Wq = Hq * D;
   const size_t row = (size_t)b * R + r;
   int32_t* ur = urow + row * (size_t)L;
-  if (status[b] != 0) {                           // stopped sequence: nothing to attend (block-uniform)
-    if (tid == 0) ntok[row] = 0;
+  // ---- the append decision (block-uniform: every thread sums the same LDS values in the same order)
+  const int t = seq_len[b];                       // tokens in the cache before this one
+  const int nc0 = num_closed[b];
+  const int32_t* cs = chunk_start + (size_t)b * (Cmax + 1);
+  const int c00 = cs[nc0];
+  int code = status[b] != 0 ? -1 : (t >= L ? 1 : 0);   // -1 stopped before, 1 cache full, 2 table full
+  const T* kn = k + (size_t)b * Wk;
+  T* kc = k_cache + (size_t)b * L * Wk;
+  float dot = 0.f, na = 0.f, nb = 0.f;
+  if (code == 0 && t > 0) {
+    for (int x = tid; x < Wk; x += kRouteThreads) {
+      const float a = to_f(kc[(size_t)(t - 1) * Wk + x]), c = to_f(kn[x]);
+      dot = fmaf(a, c, dot);
+      na = fmaf(a, a, na);
+      nb = fmaf(c, c, nb);
+    }
+  }
+  dot = wave_add(dot);
+  na = wave_add(na);
+  nb = wave_add(nb);
+  if (lane == 0) { red[0][wv] = dot; red[1][wv] = na; red[2][wv] = nb; }
+  __syncthreads();
+  dot = na = nb = 0.f;
+#pragma unroll
+  for (int w = 0; w < kRouteThreads / 64; ++w) { dot += red[0][w]; na += red[1][w]; nb += red[2][w]; }
+  const float sim = (t > 0 && na > 0.f && nb > 0.f) ? dot / (sqrtf(na) * sqrtf(nb)) : 1.0f;
+  const int n_open = t - c00;
+  const bool cut = code == 0 && t > 0 && ((n_open >= lo && sim < tau) || n_open >= hi);
+  if (cut && nc0 + 1 > Cmax) code = 2;
+  if (code != 0) {                                // stopped: nothing to attend, the state stays
+    if (tid == 0) {
+      ntok[row] = 0;
+      if (r == 0) pend[b] = make_int4(code, 0, 0, 0);
+    }
     return;
   }
-  const int t_end = seq_len[b];                   // tokens in the cache, the new one included
-  const int nc = num_closed[b];
-  const int32_t* cs = chunk_start + (size_t)b * (Cmax + 1);
-  const int c0 = cs[nc];
+  const int nc = nc0 + (cut ? 1 : 0);             // closed chunks with this token
+  const int c0 = cut ? t : c00;                   // the open chunk's first token
+  const int t_end = t + 1;                        // tokens in the cache, this one included
+  if (cut) {
+    const float inv_c = 1.0f / sqrtf((float)n_open);
+    const float* kr = k_run + ((size_t)b * Hkv + g) * D;
+    for (int x = tid; x < D; x += kRouteThreads) {
+      const float a = kr[x] * inv_c;
+      ksn[x] = a;
+      if (owner) k_sum[(((size_t)b * Cmax + nc0) * Hkv + g) * D + x] = a;
+    }
+  }
+  if (owner) {
+    const T* vn = v + (size_t)b * Wk;
+    T* vc = v_cache + (size_t)b * L * Wk;
+    for (int x = tid; x < D; x += kRouteThreads) {
+      kc[(size_t)t * Wk + g * D + x] = kn[g * D + x];
+      vc[(size_t)t * Wk + g * D + x] = vn[g * D + x];
+    }
+  }
+  if (r == 0 && tid == 0) pend[b] = make_int4(0, cut ? 1 : 0, t, nc0);
+  // the open chunk's query summary with this token
   const float inv = 1.0f / sqrtf((float)(t_end - c0));
-  for (int x = tid; x <= nc; x += kRouteThreads) cs_l[x] = cs[x];   // nc <= kDecodeMaxChunks
+  const float* qr = q_run + (size_t)b * Wq;
+  const T* qn = q + (size_t)b * Wq;
+  for (int x = tid; x <= nc0; x += kRouteThreads) cs_l[x] = cs[x];  // nc0 <= Cmax <= kDecodeMaxChunks
+  if (cut && tid == 0) cs_l[nc] = c0;
   for (int x = tid; x < D; x += kRouteThreads) {
     float a;
     if constexpr (GROUPED) {
       a = 0.f;
-      for (int hh = 0; hh < G; ++hh) a += q_run[((size_t)b * Hq + g * G + hh) * D + x] * inv;
+      for (int hh = 0; hh < G; ++hh) {
+        const int y = (g * G + hh) * D + x;
+        a += (cut ? to_f(qn[y]) : qr[y] + to_f(qn[y])) * inv;
+      }
     } else {
-      a = q_run[((size_t)b * Hq + r) * D + x] * inv;
+      const int y = r * D + x;
+      a = (cut ? to_f(qn[y]) : qr[y] + to_f(qn[y])) * inv;
     }
     qv[x] = a;
   }
@@ -213,10 +208,11 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(
     // key summaries read across lanes: LS lanes x 16 bytes per summary row, RS rows per load, 16
     // loads in flight per wave; each lane's partial dot product summed over its row's lanes
     constexpr int LS = D / 4, RS = 64 / LS;
-    const int wv = tid >> 6, sr = lane / LS, sp = lane % LS;
+    const int sr = lane / LS, sp = lane % LS;
     const float4 q4 = *reinterpret_cast<const float4*>(&qv[4 * sp]);
-    const int per_wave = (nc + kRouteThreads / 64 - 1) / (kRouteThreads / 64);
-    const int j_lo = wv * per_wave, j_hi = min(nc, j_lo + per_wave);
+    // chunks closed before this token: summaries in memory
+    const int per_wave = (nc0 + kRouteThreads / 64 - 1) / (kRouteThreads / 64);
+    const int j_lo = wv * per_wave, j_hi = min(nc0, j_lo + per_wave);
     for (int j0 = j_lo; j0 < j_hi; j0 += 16 * RS) {
       float4 kv[16];
 #pragma unroll
@@ -235,6 +231,15 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(
         const int j = j0 + x * RS + sr;
         if (sp == LS - 1 && j < j_hi) scores[j] = a;
       }
+    }
+    if (cut && wv == kRouteThreads / 64 - 1) {   // the chunk this token closes, from LDS, same arithmetic
+      const float4 k4 = *reinterpret_cast<const float4*>(&ksn[4 * sp]);
+      float a = q4.x * k4.x;
+      a = fmaf(q4.y, k4.y, a);
+      a = fmaf(q4.z, k4.z, a);
+      a = fmaf(q4.w, k4.w, a);
+      a = row_sum<LS>(a);
+      if (sp == LS - 1 && sr == 0) scores[nc0] = a;
     }
   }
   __syncthreads();
@@ -593,8 +598,10 @@ __global__ __launch_bounds__(64) void decode_attend_kernel(
 // flight at once.
 template <typename T, int D, bool GROUPED>
 __global__ __launch_bounds__(64) void decode_combine_kernel(
-    const float* __restrict__ part, const int32_t* __restrict__ ntok, const int32_t* __restrict__ status,
-    int Hq, int Hkv, int NS, T* __restrict__ out) {
+    const float* __restrict__ part, const int32_t* __restrict__ ntok, int Hq, int Hkv, int NS, T* __restrict__ out,
+    const T* __restrict__ q, const T* __restrict__ k, const int4* __restrict__ pend, int Cmax,
+    int32_t* __restrict__ seq_len, int32_t* __restrict__ num_closed, int32_t* __restrict__ chunk_start,
+    float* __restrict__ q_run, float* __restrict__ k_run, int32_t* __restrict__ status) {
   constexpr int XPL = (D + 63) / 64;              // output columns per lane
   __shared__ float wgt[kDecodeMaxSlices];
   const int bh = blockIdx.x, lane = threadIdx.x;
@@ -603,7 +610,31 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
   const size_t row = (size_t)b * (GROUPED ? Hkv : Hq) + (GROUPED ? h / G : h);
   const int n = ntok[row];
   T* op = out + (size_t)bh * D;
-  if (status[b] != 0 || n == 0) {                 // stopped sequence: zeros
+  // commit the token's append to the state (no other kernel of the step reads these fields after the
+  // routing launch): this head's query sum, the KV head's key sum (first head of its group), the
+  // sequence's counters (head 0)
+  const int4 pd = pend[b];
+  if (pd.x == 0) {
+    const bool cut = pd.y != 0;
+    float* qr = q_run + (size_t)bh * D;
+    const T* qn = q + (size_t)bh * D;
+    for (int x = lane; x < D; x += 64) qr[x] = cut ? to_f(qn[x]) : qr[x] + to_f(qn[x]);
+    if (h % G == 0) {
+      float* kr = k_run + ((size_t)b * Hkv + h / G) * D;
+      const T* kn = k + ((size_t)b * Hkv + h / G) * D;
+      for (int x = lane; x < D; x += 64) kr[x] = cut ? to_f(kn[x]) : kr[x] + to_f(kn[x]);
+    }
+    if (h == 0 && lane == 0) {
+      seq_len[b] = pd.z + 1;
+      if (cut) {
+        num_closed[b] = pd.w + 1;
+        chunk_start[(size_t)b * (Cmax + 1) + pd.w + 1] = pd.z;
+      }
+    }
+  } else if (pd.x > 0 && h == 0 && lane == 0) {
+    status[b] = pd.x;
+  }
+  if (n == 0) {                                   // stopped sequence (no kept token): zeros
     for (int x = lane; x < D; x += 64) from_f(0.f, op[x]);
     return;
   }
@@ -735,16 +766,13 @@ template <typename T, int D, bool GROUPED>
 hipError_t step_d(const DecodeDims& p, const DecodePtrs& s, const void* q, const void* k, const void* v, int lo,
                   int hi, float tau, int topk, float scale, void* out, int32_t* kept, const DecodeWork& w,
                   hipStream_t stream) {
-  hipLaunchKernelGGL(decode_append_kernel<T>, dim3(p.B), dim3(kAppendThreads), 0, stream, (const T*)q, (const T*)k,
-                     (const T*)v, (T*)s.k_cache, (T*)s.v_cache, s.seq_len, s.num_closed, s.chunk_start, s.k_sum,
-                     s.q_run, s.k_run, s.status, p.Hq, p.Hkv, D, p.L, p.Cmax, lo, hi, tau);
+  const int R = GROUPED ? p.Hkv : p.Hq;
+  hipLaunchKernelGGL((decode_route_kernel<T, D, GROUPED>), dim3(p.B * R), dim3(kRouteThreads), 0, stream,
+                     (const T*)q, (const T*)k, (const T*)v, (T*)s.k_cache, (T*)s.v_cache, s.k_sum, s.q_run, s.k_run,
+                     s.seq_len, s.num_closed, s.chunk_start, s.status, p.Hq, p.Hkv, p.Cmax, p.L, topk, lo, hi, tau,
+                     w.urow, w.ntok, kept, (int4*)w.pend);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int R = GROUPED ? p.Hkv : p.Hq;
-  hipLaunchKernelGGL((decode_route_kernel<D, GROUPED>), dim3(p.B * R), dim3(kRouteThreads), 0, stream, s.q_run, s.k_sum,
-                     s.seq_len, s.num_closed, s.chunk_start, s.status, p.Hq, p.Hkv, p.Cmax, p.L, topk, w.urow,
-                     w.ntok, kept);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
   // heads per attention wave: the whole group when routing per KV head (each K/V row read once for it)
   const int G = p.Hq / p.Hkv;
   const int gh = !GROUPED ? 1 : (G == 8 ? 8 : G == 4 ? 4 : G == 2 ? 2 : 1);
@@ -767,7 +795,8 @@ hipError_t step_d(const DecodeDims& p, const DecodePtrs& s, const void* q, const
 #undef DHSA_ATTEND
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL((decode_combine_kernel<T, D, GROUPED>), dim3(p.B * p.Hq), dim3(64), 0, stream, w.part, w.ntok,
-                     s.status, p.Hq, p.Hkv, w.NS, (T*)out);
+                     p.Hq, p.Hkv, w.NS, (T*)out, (const T*)q, (const T*)k, (const int4*)w.pend, p.Cmax, s.seq_len,
+                     s.num_closed, s.chunk_start, s.q_run, s.k_run, s.status);
   return hipGetLastError();
 }
 

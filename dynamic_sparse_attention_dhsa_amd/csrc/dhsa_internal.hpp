@@ -74,6 +74,7 @@ struct DecodeWork {                               // carved from the caller's wo
   int32_t* urow;                                  // [B * rows, L]: cache row of each kept token, kept order
   int32_t* ntok;                                  // [B * rows]
   float* part;                                    // [B * Hq * NS, d + 2]
+  int32_t* pend;                                  // [B, 4]: the token's append, committed by the combine
   int NS;                                         // slices per (sequence, q head)
 };
 hipError_t launch_decode_step(const DecodeDims& p, const DecodePtrs& s, const void* q, const void* k, const void* v,

@@ -152,6 +152,35 @@ def test_full_cache_stops_the_sequence():
     assert np.abs(outs[:10, 0] - o_out).max() <= OUT_ATOL["bf16"]
 
 
+@pytest.mark.parametrize("grouped", [False, True])
+def test_full_chunk_table_stops_only_that_sequence(grouped):
+    """Two sequences, table of C closed chunks: C is the first sequence's final count (it fills the table
+    exactly and goes on), the second reaches a (C + 1)-th cut mid-run and stops there (status 2): its
+    outputs are zeros from that token on, its state stays as it was; the first is unaffected."""
+    seqs = [SeqSpec(220, ("uniform", 8, 30), 0, 0), SeqSpec(220, ("uniform", 8, 30), 0, 0)]
+    Hq, Hkv, d, seed, P, lo, hi, tau, topk = 4, 2, 64, 68, 120, 8, 32, 0.5, 2
+    w = W.make_workload(seqs, Hq, Hkv, d, "bf16", seed=seed, name="decode")
+    qf, kf, vf = w.q_f32(), w.k_f32(), w.v_f32()
+    cs = w.cu_seqlens
+    scale = 1.0 / np.sqrt(d)
+    ref = [oracle.decode_sequence(qf[cs[b]:cs[b + 1]], kf[cs[b]:cs[b + 1]], vf[cs[b]:cs[b + 1]], lo, hi, tau,
+                                  topk, scale, first_output=P, grouped=grouped) for b in range(2)]
+    starts = [r[1] for r in ref]
+    C = len(starts[0]) - 1
+    assert len(starts[1]) - 1 > C and starts[1][C + 1] >= P, "the seed must give a mid-run stop"
+    t_stop = starts[1][C + 1]                   # the token whose cut would close chunk C + 1
+    w2, outs, _, state, status, _ = _run(seqs, Hq, Hkv, d, "bf16", seed, P, lo, hi, tau, topk, grouped, C=C)
+    assert status.tolist() == [0, 2]
+    n_ok = t_stop - P
+    assert np.abs(outs[:, 0] - ref[0][0]).max() <= OUT_ATOL["bf16"]
+    assert np.abs(outs[:n_ok, 1] - ref[1][0][:n_ok]).max() <= OUT_ATOL["bf16"]
+    assert np.all(outs[n_ok:, 1] == 0.0)
+    assert int(state.seq_len[0].item()) == 220 and int(state.seq_len[1].item()) == t_stop
+    assert [int(x) for x in state.num_closed.cpu()] == [C, C]
+    for b in range(2):
+        assert state.chunk_start[b, :C + 1].cpu().numpy().tolist() == starts[b][:C + 1]
+
+
 @pytest.mark.slow
 def test_decode_32k_context():
     seqs = [SeqSpec(32768 + 24, ("uniform", 64, 512), 0, 0)]
