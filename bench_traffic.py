@@ -84,11 +84,14 @@ def main() -> int:
     work = tempfile.mkdtemp(prefix="dhsa_traffic_")
     bench = [sys.executable, "-u", "bench.py", "--config", str(args.config), "--steps", "2", "--warmup", "1",
              "--no-cpu-baseline"]
+    # bench.py's first 1 + 2 prefill launches are the step's (warm-up, then timed); the cold-cache
+    # repetitions and the token-budget launches that follow run other lists or other cache states
+    step_launches = 3
     copy = [sys.executable, "-u", "-c", COPY_SNIPPET]
     kib = {}
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         rows = rocprof_pass(counter, bench, os.path.join(work, "bench_" + counter), args.timeout)
-        vals = per_dispatch(rows, counter, lambda k: "prefill_bf16_kernel" in k)
+        vals = per_dispatch(rows, counter, lambda k: "prefill_bf16_kernel" in k)[:step_launches]
         crow = rocprof_pass(counter, copy, os.path.join(work, "copy_" + counter), args.timeout)
         cvals = per_dispatch(crow, counter, lambda k: True)
         if not vals or not cvals:

@@ -464,7 +464,7 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
   // Waves without query rows (possible when the workgroup holds several row blocks) only stage
   // tiles.  Every other wave runs the same straight-line tile body: after the last tile the QK^T of
   // the (absent) next tile reads a stale but finite K stage and is discarded.
-  f32x16 sA[2], sB[2];
+  f32x16 sA[2], sB[2] = {zero16, zero16};      // sB is first read after a skipped iteration
   if (wave_rows) {
     float dummy;
     region_a(std::true_type{}, std::false_type{}, k_st0, sA, sB, dummy);   // S^T of tile 0
@@ -482,7 +482,12 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
     const TileRef t3 = build();
     if (t2.valid) load_k(t2, k_fill);
     if (t1.valid) load_v(t1, v_fill);
-    if (wave_rows) {
+    // A tile holding no row that this wave's head keeps (a chunk kept only by other heads of the
+    // workgroup) has every score masked, and its softmax update changes nothing.  When the next tile
+    // is such a tile too, the wave skips the iteration's QK^T, softmax and PV (a wave-uniform branch
+    // on the scalar tile records); the stale scores it then leaves for the next tile are all
+    // overwritten by that tile's mask, which selects -inf for every row.
+    if (wave_rows && (t0.nval != 0 || t1.nval != 0)) {
       if (needs_mask(t0)) apply_mask(sc, t0);
       float alpha = 1.f;
       // The half with the softmax issues first when both waves of the SIMD are ready: its VALU chain
