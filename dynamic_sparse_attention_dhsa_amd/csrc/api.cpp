@@ -54,7 +54,7 @@ dhsa_status check_layout(const dhsa_layout* L, Plan* plan) {
   if (max_per_seq > DHSA_MAX_CHUNKS_PER_SEQ) return DHSA_ERR_UNSUPPORTED;
   if (plan != nullptr) {
     *plan = Plan{B, T, C, L->num_q_heads, L->num_kv_heads, L->head_dim, L->dtype,
-                 L->cu_seqlens, L->cu_chunks, L->seq_chunk_start, max_len, max_per_seq};
+                 L->cu_seqlens, L->cu_chunks, L->seq_chunk_start, max_len, max_per_seq, cc};
   }
   return DHSA_OK;
 }

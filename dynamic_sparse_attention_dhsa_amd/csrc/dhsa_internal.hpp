@@ -18,6 +18,7 @@ struct Plan {
   const int32_t* seq_chunk_start;  // device
   int32_t max_chunk_len;           // longest chunk (tokens)
   int32_t max_chunks_per_seq;      // most chunks in one sequence
+  const int32_t* h_cu_chunks;      // host mirror of cu_chunks (valid during the call)
 };
 
 // Stage 1: q_sum / k_sum (fp32).

@@ -20,7 +20,12 @@
 // Blocks are numbered so that all row tiles of one (KV head, query chunk)
 // land on the same XCD (blocks are dealt to the 8 XCDs round robin), where
 // they stream the same kept K/V through one L2; KV heads go one after
-// another across the chip, heaviest chunks first.
+// another across the chip, heaviest chunks first.  Each XCD's blocks are
+// its groups' real row tiles back to back, with no block for rows past a
+// chunk's end: the dispatcher hands blocks out in order, round robin over
+// the XCDs, so an XCD whose slots are full holds back every other one, and
+// padding blocks that make the XCDs' shares of real work differ from one
+// dispatch position to the next leave slots idle.
 //
 // Per tile and wave (32 queries x 64 keys), with v_mfma_f32_32x32x16_bf16:
 //   S^T = K Q^T      A = K rows from LDS, B = Q^T held in registers for the whole walk
@@ -36,6 +41,7 @@
 // XOR-swizzled by row so that the fragment reads hit 64 distinct banks.  An
 // iteration issues the loads of the next V and of the K after next, computes,
 // waits for its own loads and ends with one barrier.
+#include <algorithm>
 #include <type_traits>
 
 #include "dhsa_internal.hpp"
@@ -53,6 +59,7 @@ typedef void __attribute__((address_space(3))) lds_void;
 
 constexpr int kMaxWords = DHSA_MAX_WORDS;      // bitmap words per head (32 chunks each)
 constexpr int kUnion = 4;                      // bitmap row of the union (head slots use rows 0..3)
+constexpr int kCompactMaxGroups = 2048;        // (KV head, chunk) groups per XCD for compact block numbering
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleLog2 = 8.0f;           // move the running max only past 2^8
 constexpr int kBufWord3 = 0x00020000;          // gfx9 buffer resource: raw 32-bit data
@@ -122,7 +129,7 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ block_idx,
     const int32_t* __restrict__ cu_chunks, const int32_t* __restrict__ seq_chunk_start,
     uint16_t* __restrict__ out, float* __restrict__ lse, int B, int C, int T, int Hq, int Hkv,
-    long long nnz, float scale, int hp, int head_slots, int row_tiles) {
+    long long nnz, float scale, int hp, int head_slots, int row_tiles, int compact) {
   using GE = Geo<D>;
   constexpr int NW = GE::NW, NT = GE::NT, BK = GE::BK;
   // Two-stage rings, one LDS array per stage: K of the tile after next and V of the next tile load
@@ -134,22 +141,68 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t v_st1[GE::TILEB];
   __shared__ uint32_t bm[kUnion + 1][kMaxWords];            // per head slot, then their union
 
-  // ---- block -> (KV head, chunk, head slot, row tile); one XCD per (KV head, chunk)
+  // ---- block -> (KV head, chunk, head slot, row tile); group g = (KV head, chunk) on XCD g % 8
   const int G = Hq / Hkv;
   const int rb_count = NW / hp;
-  const int per_group = head_slots * row_tiles;
+  const int rows_blk = rb_count * 32;
   const int xcd = blockIdx.x & 7;
-  const int kth = blockIdx.x >> 3;
-  const int gid = (kth / per_group) * 8 + xcd;
-  if (gid >= Hkv * C) return;                              // block-uniform
-  const int sub = kth % per_group;
-  const int rt = __builtin_amdgcn_readfirstlane(sub % row_tiles);
-  const int hs = __builtin_amdgcn_readfirstlane(sub / row_tiles);
+  const int kth = blockIdx.x >> 3;                         // position among this XCD's blocks
+  const int ngroups = Hkv * C;
+  // group g holds KV head g / C and chunk C - 1 - g % C (heaviest, i.e. latest, chunks first)
+  auto group_tiles = [&](int g) __attribute__((always_inline)) {
+    const int ci = C - 1 - (g % C);
+    return head_slots * ((cu_chunks[ci + 1] - cu_chunks[ci] + rows_blk - 1) / rows_blk);
+  };
+  int gid, sub;
+  if (compact) {
+    // this XCD's groups xcd + 8 m, m < ng_x, each with its real row tiles: an exclusive scan of the
+    // per-thread tile counts (contiguous ranges of m) finds the group holding position kth
+    __shared__ int s_wsum[NW];
+    __shared__ int s_sel[2];
+    const int t0 = threadIdx.x, l0 = t0 & 63, w0 = t0 >> 6;
+    const int ng_x = ngroups > xcd ? (ngroups - xcd + 7) >> 3 : 0;
+    const int per = (ng_x + NT - 1) / NT;
+    const int m_lo = t0 * per, m_hi = min(ng_x, m_lo + per);
+    int my = 0;
+    for (int m = m_lo; m < m_hi; ++m) my += group_tiles(xcd + 8 * m);
+    int incl = my;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off);
+      if (l0 >= off) incl += o;
+    }
+    if (l0 == 63) s_wsum[w0] = incl;
+    if (t0 == 0) s_sel[0] = -1;
+    __syncthreads();
+    for (int x = 0; x < w0; ++x) incl += s_wsum[x];
+    if (kth >= incl - my && kth < incl) {
+      int acc = incl - my;
+      for (int m = m_lo; m < m_hi; ++m) {
+        const int t = group_tiles(xcd + 8 * m);
+        if (kth < acc + t) { s_sel[0] = m; s_sel[1] = kth - acc; break; }
+        acc += t;
+      }
+    }
+    __syncthreads();
+    const int msel = __builtin_amdgcn_readfirstlane(s_sel[0]);
+    if (msel < 0) return;                                  // block-uniform: past this XCD's row tiles
+    gid = xcd + 8 * msel;
+    sub = __builtin_amdgcn_readfirstlane(s_sel[1]);
+  } else {
+    // every group padded to row_tiles x head_slots blocks (too many groups for the scan above)
+    const int per_group = head_slots * row_tiles;
+    gid = (kth / per_group) * 8 + xcd;
+    if (gid >= ngroups) return;                            // block-uniform
+    sub = kth % per_group;
+  }
   const int gk = __builtin_amdgcn_readfirstlane(gid / C);  // (integer division runs on the VALU)
-  const int i = __builtin_amdgcn_readfirstlane(C - 1 - (gid % C));   // heaviest (latest) chunks first
+  const int i = __builtin_amdgcn_readfirstlane(C - 1 - (gid % C));
   const int s_i = cu_chunks[i], e_i = cu_chunks[i + 1];
-  const int q0 = s_i + rt * rb_count * 32;
-  if (q0 >= e_i) return;                                   // block-uniform
+  const int tiles_i = compact ? (e_i - s_i + rows_blk - 1) / rows_blk : row_tiles;
+  const int rt = __builtin_amdgcn_readfirstlane(sub % tiles_i);
+  const int hs = __builtin_amdgcn_readfirstlane(sub / tiles_i);
+  const int q0 = s_i + rt * rows_blk;
+  if (q0 >= e_i) return;                                   // block-uniform (padded blocks only)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -544,12 +597,30 @@ hipError_t launch_d(const Plan& p, const void* q, const void* k, const void* v, 
   const int row_tiles = (p.max_chunk_len + rows_per_block - 1) / rows_per_block;
   const int head_slots = G / hp;
   const long long groups = (long long)p.Hkv * p.C;
-  const long long blocks = (groups + 7) / 8 * 8 * head_slots * row_tiles;
+  // Compact numbering (each XCD's real row tiles only) while the kernel's per-block scan over an XCD's
+  // groups stays short; the grid then covers the XCD with the most tiles.  Group g = gk C + (C-1-i)
+  // sits on XCD g % 8, so the tiles of the chunks with (C-1-i) % 8 == r land on XCD (gk C + r) % 8.
+  const bool compact = (groups + 7) / 8 <= kCompactMaxGroups;
+  long long blocks;
+  if (compact) {
+    long long by_res[8] = {0, 0, 0, 0, 0, 0, 0, 0}, tiles_x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int ci = 0; ci < p.C; ++ci) {
+      const int n = p.h_cu_chunks[ci + 1] - p.h_cu_chunks[ci];
+      by_res[(p.C - 1 - ci) & 7] += (long long)head_slots * ((n + rows_per_block - 1) / rows_per_block);
+    }
+    for (int gk = 0; gk < p.Hkv; ++gk)
+      for (int r = 0; r < 8; ++r) tiles_x[((long long)gk * p.C + r) & 7] += by_res[r];
+    long long tmax = 0;
+    for (int x = 0; x < 8; ++x) tmax = std::max(tmax, tiles_x[x]);
+    blocks = 8 * tmax;
+  } else {
+    blocks = (groups + 7) / 8 * 8 * head_slots * row_tiles;
+  }
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   auto kern = lse != nullptr ? prefill_bf16_kernel<D, true> : prefill_bf16_kernel<D, false>;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(GE::NT), 0, stream, (const uint16_t*)q, (const uint16_t*)k,
                      (const uint16_t*)v, row_ptr, block_idx, p.cu_chunks, p.seq_chunk_start, (uint16_t*)out, lse,
-                     p.B, p.C, p.T, p.Hq, p.Hkv, (long long)nnz, scale, hp, head_slots, row_tiles);
+                     p.B, p.C, p.T, p.Hq, p.Hkv, (long long)nnz, scale, hp, head_slots, row_tiles, compact ? 1 : 0);
   return hipGetLastError();
 }
 

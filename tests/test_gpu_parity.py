@@ -219,6 +219,17 @@ def test_small_grouped_routing_and_end_to_end(name):
     check_end_to_end(case)
 
 
+def test_many_groups_take_the_padded_block_numbering():
+    """More than 2048 (KV head, chunk) groups per XCD: the prefill kernel numbers its blocks with every
+    group padded to the longest chunk's row tiles instead of compacting each XCD's real row tiles (the
+    per-block scan over an XCD's groups would grow too long).  Whole path against the oracle."""
+    w = small([SeqSpec(2100, ("uniform", 1, 7), 3, 0) for _ in range(8)], 4, 4, 64, "bf16", 21, "many_groups")
+    assert (w.num_kv_heads * w.total_chunks + 7) // 8 > 2048
+    case = Case(w)
+    check_attention(case)
+    check_end_to_end(case)
+
+
 def test_budget_extremes():
     w = small([SeqSpec(800, ("uniform", 20, 80), 0, 2), SeqSpec(500, ("uniform", 10, 60), 0, 0)], 4, 2, 128, "bf16",
               21, "extremes")
