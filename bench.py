@@ -400,7 +400,8 @@ def main() -> int:
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel" if bf16 else "prefill_f32_kernel",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": traffic_record(w.name) if bf16 else None,
+                     # the committed counter record is of the per-q-head lists (bench_traffic.py)
+                     "traffic": traffic_record(w.name) if bf16 and not grouped else None,
                      "algorithmic_flops_per_launch": F3},
         "stages": {
             "t_summarize_ms": t1 * 1e3, "t_route_ms": t2 * 1e3, "t_prefill_ms": t3 * 1e3,
