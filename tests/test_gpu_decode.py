@@ -181,6 +181,35 @@ def test_full_chunk_table_stops_only_that_sequence(grouped):
         assert state.chunk_start[b, :C + 1].cpu().numpy().tolist() == starts[b][:C + 1]
 
 
+def _draw_decode_case(i: int):
+    """Seeded random decode setting: 1-3 equal-length sequences, head layout, head dim and dtype, the
+    chunking rule, the prefix length (0 included) and the budget (0 to past every closed chunk)."""
+    rng = np.random.default_rng(8000 + i)
+    B = int(rng.integers(1, 4))
+    length = int(rng.integers(60, 400))
+    lo = int(rng.integers(1, 24))
+    hi = int(rng.integers(lo, lo + 80))
+    seqs = [SeqSpec(length, ("uniform", lo, hi), 0, 0) for _ in range(B)]
+    Hkv = int(rng.integers(1, 4))
+    G = int(rng.choice([1, 2, 3, 4, 8]))
+    dt = "f32" if rng.random() < 0.25 else "bf16"
+    d = int(rng.choice([64, 128] if dt == "f32" else [64, 128, 256]))
+    P = 0 if rng.random() < 0.2 else int(rng.integers(1, length - 8))
+    topk = int(rng.integers(0, 12))
+    tau = float(rng.choice([0.3, 0.5, 0.7]))
+    grouped = bool(rng.random() < 0.5) and G > 1
+    return (seqs, Hkv * G, Hkv, d, dt, 8100 + i, P, lo, hi, tau, topk), grouped
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_decode_settings(i):
+    args, grouped = _draw_decode_case(i)
+    seqs, Hq, Hkv, d, dt, seed, P, lo, hi, tau, topk = args
+    print(f"[decode sweep {i}] B={len(seqs)} len={seqs[0].length} Hq/Hkv={Hq}/{Hkv} d={d} {dt} P={P} "
+          f"lo={lo} hi={hi} tau={tau} topk={topk} grouped={grouped}", flush=True)
+    _check(*args, grouped=grouped)
+
+
 @pytest.mark.slow
 def test_decode_32k_context():
     seqs = [SeqSpec(32768 + 24, ("uniform", 64, 512), 0, 0)]
