@@ -13,8 +13,11 @@
 // 4) times 4 / HP blocks of 32 query rows, so one K/V tile staged in LDS feeds
 // every q head of the group that keeps it.  The workgroup walks the union of
 // its heads' kept chunks in ascending order (per-head bitmaps in LDS); a
-// head's scores on a chunk it does not keep are masked.  Key tiles hold 64
-// keys and never cross a chunk boundary; keys past the chunk end or past the
+// head's scores on a chunk it does not keep are masked, and a wave skips the
+// iterations on runs of tiles its head keeps none of.  Key tiles hold 64 keys
+// in groups of a few rows; a group never crosses a chunk boundary, a tile may
+// (the kept chunks before the diagonal are packed back to back, the diagonal
+// chunk takes tiles of its own); rows past a chunk's end or past the
 // diagonal are masked.
 //
 // Blocks are numbered so that all row tiles of one (KV head, query chunk)
@@ -25,7 +28,9 @@
 // chunk's end: the dispatcher hands blocks out in order, round robin over
 // the XCDs, so an XCD whose slots are full holds back every other one, and
 // padding blocks that make the XCDs' shares of real work differ from one
-// dispatch position to the next leave slots idle.
+// dispatch position to the next leave slots idle.  (Past 2048 groups per
+// XCD, where each block's scan over its XCD's groups would grow long, every
+// group is padded to the longest chunk's row tiles instead.)
 //
 // Per tile and wave (32 queries x 64 keys), with v_mfma_f32_32x32x16_bf16:
 //   S^T = K Q^T      A = K rows from LDS, B = Q^T held in registers for the whole walk
