@@ -119,6 +119,21 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
+def _on_gpu(t: torch.Tensor) -> bool:
+    """A GPU tensor on the current device (the library launches on that device's current stream)."""
+    return t.is_cuda and t.device.index == torch.cuda.current_device()
+
+
+def _require(t: Optional[torch.Tensor], name: str, shape, dtype: torch.dtype) -> None:
+    """A caller-supplied tensor the kernels read or write in full: contiguous, of this dtype and exact
+    shape, on the current GPU (None: the binding allocates it)."""
+    if t is None:
+        return
+    if not _on_gpu(t) or t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise DhsaError(2, name, f"expected a contiguous {dtype} tensor {list(shape)} on the current GPU, "
+                                 f"got {t.dtype} {list(t.shape)} on {t.device}")
+
+
 def _host_i32(a) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
 
@@ -139,6 +154,8 @@ class Layout:
             raise DhsaError(5, "Layout", f"unsupported dtype {dtype}")
         self.dtype = dtype
         self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         self.d_cu_seqlens = torch.from_numpy(self.h_cu_seqlens).to(self.device)
         self.d_cu_chunks = torch.from_numpy(self.h_cu_chunks).to(self.device)
         self.d_seq_chunk_start = torch.from_numpy(self.h_seq_chunk_start).to(self.device)
@@ -156,8 +173,10 @@ class Layout:
         _check(load_library().dhsa_validate_layout(ctypes.byref(self.struct)), "dhsa_validate_layout")
 
     def _check_tensor(self, t: torch.Tensor, heads: int, name: str) -> None:
-        if not t.is_cuda:
-            raise DhsaError(1, name, "tensor is not on the GPU")
+        if self.device.index != torch.cuda.current_device():
+            raise DhsaError(1, name, f"layout is on {self.device}, the current device is cuda:{torch.cuda.current_device()}")
+        if not _on_gpu(t):
+            raise DhsaError(1, name, "tensor is not on the current GPU")
         if t.dtype != self.dtype:
             raise DhsaError(2, name, f"dtype {t.dtype} != layout dtype {self.dtype}")
         if tuple(t.shape) != (self.total_tokens, heads, self.head_dim) or not t.is_contiguous():
@@ -216,6 +235,8 @@ def chunk_summarize(layout: Layout, q: torch.Tensor, k: torch.Tensor,
     layout._check_tensor(q, layout.num_q_heads, "q")
     layout._check_tensor(k, layout.num_kv_heads, "k")
     C = layout.total_chunks
+    _require(q_sum, "q_sum", (C, layout.num_q_heads, layout.head_dim), torch.float32)
+    _require(k_sum, "k_sum", (C, layout.num_kv_heads, layout.head_dim), torch.float32)
     if q_sum is None:
         q_sum = torch.empty((C, layout.num_q_heads, layout.head_dim), dtype=torch.float32, device=q.device)
     if k_sum is None:
@@ -231,9 +252,10 @@ def route(layout: Layout, plan: RoutePlan, q_sum: torch.Tensor, k_sum: torch.Ten
     by its query heads): kept key chunks, int32 [Hq, nnz], rows ascending with the diagonal last."""
     if block_idx is None:
         block_idx = torch.empty((layout.num_q_heads, plan.nnz), dtype=torch.int32, device=q_sum.device)
-    for t, name in ((q_sum, "q_sum"), (k_sum, "k_sum")):
-        if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
-            raise DhsaError(2, name, "expected a contiguous float32 GPU tensor")
+    C = layout.total_chunks
+    _require(q_sum, "q_sum", (C, layout.num_q_heads, layout.head_dim), torch.float32)
+    _require(k_sum, "k_sum", (C, layout.num_kv_heads, layout.head_dim), torch.float32)
+    _require(block_idx, "block_idx", (layout.num_q_heads, plan.nnz), torch.int32)
     name = "dhsa_route_grouped" if grouped else "dhsa_route"
     _check(getattr(load_library(), name)(ctypes.byref(layout.struct), _ptr(q_sum), _ptr(k_sum),
                                          _ptr(plan.d_row_ptr), plan.h_row_ptr.ctypes.data, plan.nnz,
@@ -250,9 +272,10 @@ def route_tokens(layout: Layout, plan: TokenPlan, q_sum: torch.Tensor, k_sum: to
         raise DhsaError(2, "route_tokens", "needs a TokenPlan")
     if block_idx is None:
         block_idx = torch.empty((layout.num_q_heads, plan.nnz), dtype=torch.int32, device=q_sum.device)
-    for t, name in ((q_sum, "q_sum"), (k_sum, "k_sum")):
-        if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
-            raise DhsaError(2, name, "expected a contiguous float32 GPU tensor")
+    C = layout.total_chunks
+    _require(q_sum, "q_sum", (C, layout.num_q_heads, layout.head_dim), torch.float32)
+    _require(k_sum, "k_sum", (C, layout.num_kv_heads, layout.head_dim), torch.float32)
+    _require(block_idx, "block_idx", (layout.num_q_heads, plan.nnz), torch.int32)
     _check(load_library().dhsa_route_tokens(ctypes.byref(layout.struct), _ptr(q_sum), _ptr(k_sum),
                                             _ptr(plan.d_token_budget), plan.h_token_budget.ctypes.data,
                                             _ptr(plan.d_row_ptr), plan.h_row_ptr.ctypes.data, plan.nnz,
@@ -267,9 +290,9 @@ def sparse_prefill(layout: Layout, plan: RoutePlan, q: torch.Tensor, k: torch.Te
     layout._check_tensor(q, layout.num_q_heads, "q")
     layout._check_tensor(k, layout.num_kv_heads, "k")
     layout._check_tensor(v, layout.num_kv_heads, "v")
-    if block_idx.dtype != torch.int32 or not block_idx.is_cuda or tuple(block_idx.shape) != (layout.num_q_heads,
-                                                                                              plan.nnz):
-        raise DhsaError(2, "block_idx", f"expected int32 GPU tensor [{layout.num_q_heads}, {plan.nnz}]")
+    _require(block_idx, "block_idx", (layout.num_q_heads, plan.nnz), torch.int32)
+    _require(out, "out", (layout.total_tokens, layout.num_q_heads, layout.head_dim), layout.dtype)
+    _require(lse, "lse", (layout.num_q_heads, layout.total_tokens), torch.float32)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(layout.head_dim)
     if out is None:
@@ -327,7 +350,7 @@ def adjacent_similarity(k: torch.Tensor, cu_seqlens, tau: float, sim: Optional[t
     """dhsa_adjacent_similarity: sim float32 [T] (cosine of adjacent key rows over all KV heads, 1 at
     sequence starts and zero rows) and cut_bits int64 [ceil(T/64)] (bit t set when sim[t] < tau).
     ``cu_seqlens``: a SeqLayout, or host offsets (copied to the device on each call)."""
-    if not k.is_cuda or k.dim() != 3 or not k.is_contiguous():
+    if not _on_gpu(k) or k.dim() != 3 or not k.is_contiguous():
         raise DhsaError(2, "k", "expected a contiguous GPU tensor [T, Hkv, d]")
     if k.dtype == torch.bfloat16:
         code = DHSA_BF16
@@ -343,6 +366,9 @@ def adjacent_similarity(k: torch.Tensor, cu_seqlens, tau: float, sim: Optional[t
         cut_bits = torch.empty((T + 63) // 64, dtype=torch.int64, device=k.device)
     if sim.numel() < T or cut_bits.numel() < (T + 63) // 64:
         raise DhsaError(2, "sim/cut_bits", "output buffers too small")
+    for t, name, dt in ((sim, "sim", torch.float32), (cut_bits, "cut_bits", torch.int64)):
+        if not _on_gpu(t) or t.dtype != dt or not t.is_contiguous():
+            raise DhsaError(2, name, f"expected a contiguous {dt} tensor on the current GPU")
     _check(load_library().dhsa_adjacent_similarity(sl.num_seqs, T, k.shape[1], k.shape[2], code,
                                                    _ptr(sl.d_cu_seqlens), sl.h_cu_seqlens.ctypes.data, _ptr(k),
                                                    float(tau), _ptr(sim), _ptr(cut_bits), _stream()),
@@ -355,7 +381,7 @@ def chunk_boundaries(cut_bits: torch.Tensor, cu_seqlens, lo: int, hi: int,
                      ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """dhsa_chunk_boundaries: device cu_chunks int32 [T+1] (entries 0..C valid), seq_chunk_start
     int32 [B+1] and num_chunks int32 [1] (``out`` supplies them preallocated)."""
-    if not cut_bits.is_cuda or cut_bits.dtype != torch.int64:
+    if not _on_gpu(cut_bits) or cut_bits.dtype != torch.int64:
         raise DhsaError(2, "cut_bits", "expected an int64 GPU tensor")
     sl = _seq_layout(cu_seqlens, cut_bits.device)
     T = sl.total_tokens
@@ -366,6 +392,9 @@ def chunk_boundaries(cut_bits: torch.Tensor, cu_seqlens, lo: int, hi: int,
                torch.empty(sl.num_seqs + 1, dtype=torch.int32, device=cut_bits.device),
                torch.empty(1, dtype=torch.int32, device=cut_bits.device))
     cu_chunks, scs, nch = out
+    _require(cu_chunks, "cu_chunks", (T + 1,), torch.int32)
+    _require(scs, "seq_chunk_start", (sl.num_seqs + 1,), torch.int32)
+    _require(nch, "num_chunks", (1,), torch.int32)
     _check(load_library().dhsa_chunk_boundaries(sl.num_seqs, T, _ptr(sl.d_cu_seqlens), sl.h_cu_seqlens.ctypes.data,
                                                 _ptr(cut_bits), int(lo), int(hi), _ptr(cu_chunks), _ptr(scs),
                                                 _ptr(nch), _stream()), "dhsa_chunk_boundaries")
@@ -423,7 +452,13 @@ class DecodeState:
             self._ws[key] = torch.empty(n, dtype=torch.uint8, device=self.device)
         return self._ws[key]
 
+    def _check_device(self) -> None:
+        if not _on_gpu(self.k_cache):
+            raise DhsaError(1, "decode state", f"state is on {self.k_cache.device}, the current device is "
+                                               f"cuda:{torch.cuda.current_device()}")
+
     def load_prefix(self, layout: "Layout", q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> None:
+        self._check_device()
         layout._check_tensor(q, layout.num_q_heads, "q")
         layout._check_tensor(k, layout.num_kv_heads, "k")
         layout._check_tensor(v, layout.num_kv_heads, "v")
@@ -433,11 +468,14 @@ class DecodeState:
     def step(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lo: int, hi: int, tau: float, topk: int,
              grouped: bool = False, softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
              kept: Optional[torch.Tensor] = None) -> torch.Tensor:
+        self._check_device()
         B = self.seq_len.numel()
         for t, name, heads in ((q, "q", self.num_q_heads), (k, "k", self.num_kv_heads), (v, "v", self.num_kv_heads)):
-            if not t.is_cuda or t.dtype != self.dtype or tuple(t.shape) != (B, heads, self.head_dim) \
+            if not _on_gpu(t) or t.dtype != self.dtype or tuple(t.shape) != (B, heads, self.head_dim) \
                     or not t.is_contiguous():
-                raise DhsaError(2, name, f"expected contiguous {self.dtype} [{B}, {heads}, {self.head_dim}] on the GPU")
+                raise DhsaError(2, name, f"expected contiguous {self.dtype} [{B}, {heads}, {self.head_dim}] on the current GPU")
+        _require(out, "out", (B, self.num_q_heads, self.head_dim), self.dtype)
+        _require(kept, "kept", (B, self.num_q_heads, topk), torch.int32)
         if softmax_scale is None:
             softmax_scale = 1.0 / math.sqrt(self.head_dim)
         if out is None:

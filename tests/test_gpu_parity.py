@@ -230,6 +230,37 @@ def test_many_groups_take_the_padded_block_numbering():
     check_end_to_end(case)
 
 
+def test_binding_refuses_mis_sized_buffers():
+    """Caller-supplied tensors the kernels read or write in full are checked for shape, dtype and device
+    before any launch: a short output, a wrong-dtype LSE, short summaries, a mis-sized block list or
+    decode kept array raise DhsaError."""
+    case = Case(SMALL["bf16_d64_g1"]())
+    L, plan, w = case.layout, case.plan, case.w
+    bidx = torch.from_numpy(np.ascontiguousarray(case.o_bidx)).cuda()
+    short_out = torch.empty((w.total_tokens - 1, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(D.DhsaError):
+        D.sparse_prefill(L, plan, case.q, case.k, case.v, bidx, w.softmax_scale, out=short_out)
+    with pytest.raises(D.DhsaError):
+        D.sparse_prefill(L, plan, case.q, case.k, case.v, bidx, w.softmax_scale, return_lse=True,
+                         lse=torch.empty((w.num_q_heads, w.total_tokens), dtype=torch.float64, device="cuda"))
+    with pytest.raises(D.DhsaError):
+        D.sparse_prefill(L, plan, case.q, case.k, case.v, bidx[:, :-1].contiguous(), w.softmax_scale)
+    qs, ks = D.chunk_summarize(L, case.q, case.k)
+    with pytest.raises(D.DhsaError):
+        D.route(L, plan, qs[:-1].contiguous(), ks)
+    with pytest.raises(D.DhsaError):
+        D.route(L, plan, qs, ks, block_idx=torch.empty((w.num_q_heads, plan.nnz + 1), dtype=torch.int32,
+                                                       device="cuda"))
+    st = D.DecodeState(1, 4, 2, 64, torch.bfloat16, 64, 8)
+    q1 = torch.zeros((1, 4, 64), dtype=torch.bfloat16, device="cuda")
+    k1 = torch.zeros((1, 2, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(D.DhsaError):
+        st.step(q1, k1, k1, 4, 16, 0.5, 3, kept=torch.empty((1, 4, 2), dtype=torch.int32, device="cuda"))
+    with pytest.raises(D.DhsaError):
+        st.step(q1, k1, k1, 4, 16, 0.5, 3, out=torch.empty((1, 4, 64), dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+
+
 def test_budget_extremes():
     w = small([SeqSpec(800, ("uniform", 20, 80), 0, 2), SeqSpec(500, ("uniform", 10, 60), 0, 0)], 4, 2, 128, "bf16",
               21, "extremes")
