@@ -173,10 +173,10 @@ class Layout:
         _check(load_library().dhsa_validate_layout(ctypes.byref(self.struct)), "dhsa_validate_layout")
 
     def _check_tensor(self, t: torch.Tensor, heads: int, name: str) -> None:
-        if self.device.index != torch.cuda.current_device():
-            raise DhsaError(1, name, f"layout is on {self.device}, the current device is cuda:{torch.cuda.current_device()}")
         if not _on_gpu(t):
             raise DhsaError(1, name, "tensor is not on the current GPU")
+        if self.device.index != t.device.index:
+            raise DhsaError(1, name, f"layout is on {self.device}, the current device is {t.device}")
         if t.dtype != self.dtype:
             raise DhsaError(2, name, f"dtype {t.dtype} != layout dtype {self.dtype}")
         if tuple(t.shape) != (self.total_tokens, heads, self.head_dim) or not t.is_contiguous():
