@@ -621,7 +621,68 @@ def pin_budget_extremes_and_padding(O):
         assert np.allclose(a[:, h], b_[:, h], atol=1e-12) and np.allclose(la[h], lb[h], atol=1e-12)
 
 
-ALL_PINS = [pin_golden, pin_summary_closed_forms, pin_scores_bruteforce, pin_topk_bruteforce,
+def _raises_value_error(fn, *args) -> bool:
+    """True when fn(*args) raises ValueError; any other outcome (no error, another exception) is False."""
+    try:
+        fn(*args)
+    except ValueError:
+        return True
+    except Exception:  # noqa: BLE001 - a malformed layout must be refused by the check, not crash later
+        return False
+    return False
+
+
+# Layouts as (cu_seqlens, cu_chunks, seq_chunk_start).  Each malformed one breaks exactly one rule of
+# the chunk layout: the chunks of every sequence tile its token range exactly, each with >= 1 token
+# ("Long-Context Modeling with Dynamic Hierarchical Sparse Attention for On-Device LLMs", Abstract:
+# each sequence is split into variable-length chunks).  The same cases are fed to the C ABI's check.
+GOOD_LAYOUTS = {
+    "two sequences": ([0, 10, 17], [0, 4, 10, 13, 17], [0, 2, 4]),
+    "empty sequences inside a batch": ([0, 0, 5, 5], [0, 2, 5], [0, 0, 2, 2]),
+    "empty batch": ([0], [0], [0]),
+    "one-token chunks": ([0, 3], [0, 1, 2, 3], [0, 3]),
+}
+BAD_LAYOUTS = {
+    "chunk crosses a sequence boundary": ([0, 10, 17], [0, 4, 11, 13, 17], [0, 2, 4]),
+    "empty chunk": ([0, 10, 17], [0, 4, 4, 10, 17], [0, 3, 4]),
+    "chunk offsets do not start at 0": ([0, 10, 17], [1, 4, 10, 13, 17], [0, 2, 4]),
+    "token offsets do not start at 0": ([2, 10, 17], [0, 4, 10, 13, 17], [0, 2, 4]),
+    "sequence chunk starts out of order": ([0, 10, 17], [0, 4, 10, 13, 17], [0, 5, 4]),
+    "chunks stop short of the tokens": ([0, 10, 18], [0, 4, 10, 13, 17], [0, 2, 4]),
+    "a sequence ends inside a chunk": ([0, 9, 17], [0, 4, 10, 13, 17], [0, 2, 4]),
+    "chunk offsets go backwards": ([0, 10, 17], [0, 6, 4, 10, 13, 17], [0, 3, 5]),
+    "sequence offsets go backwards": ([0, 10, 4, 17], [0, 4, 10, 13, 17], [0, 2, 2, 4]),
+    "chunk count differs from the sequence table": ([0, 10, 17], [0, 4, 10, 13, 17], [0, 2, 3]),
+    "sequence tables of different lengths": ([0, 10, 17], [0, 4, 10, 13, 17], [0, 4]),
+}
+
+
+def pin_layout_validation(O):
+    """Every well-formed layout passes the oracle's layout check and the whole path runs on it; every
+    malformed one is refused with ValueError, both by the check and by the whole path (which validates
+    before anything else).  A negative chunk budget is refused by the plan and the whole path."""
+    rng = np.random.default_rng(5)
+    for name, (cs, cc, sc) in GOOD_LAYOUTS.items():
+        O.validate_layout(cs, cc, sc)
+        T, C = int(cc[-1]), len(cc) - 1
+        q, k, v = (rng.standard_normal((T, 2, 4)) for _ in range(3))
+        r = O.prefill(q, k, v, cs, cc, sc, np.ones(C, np.int32), 0.5)
+        assert r["out"].shape == (T, 2, 4) and not np.isnan(r["out"]).any(), name
+    for name, (cs, cc, sc) in BAD_LAYOUTS.items():
+        assert _raises_value_error(O.validate_layout, cs, cc, sc), f"layout check accepts: {name}"
+        T = max(int(max(cs)), int(max(cc)), 1)
+        C = max(len(cc) - 1, 1)
+        q, k, v = (rng.standard_normal((T, 2, 4)) for _ in range(3))
+        assert _raises_value_error(O.prefill, q, k, v, cs, cc, sc, np.ones(C, np.int32), 0.5), \
+            f"whole path accepts: {name}"
+    cs, cc, sc = GOOD_LAYOUTS["two sequences"]
+    q, k, v = (rng.standard_normal((17, 2, 4)) for _ in range(3))
+    for tk in ([1, 1, -1, 1], [1, 1, 1], [1, 1, 1, 1, 1]):      # a negative budget, too few and too many entries
+        assert _raises_value_error(O.route_plan, sc, np.array(tk, np.int32)), tk
+        assert _raises_value_error(O.prefill, q, k, v, cs, cc, sc, np.array(tk, np.int32), 0.5), tk
+
+
+ALL_PINS = [pin_layout_validation, pin_golden, pin_summary_closed_forms, pin_scores_bruteforce, pin_topk_bruteforce,
             pin_kept_invariants, pin_dense_special_case, pin_token_level_bruteforce, pin_row_sum_and_lse,
             pin_causality, pin_gqa_and_permutation, pin_ragged_equals_separate, pin_grouped_routing,
             pin_chunking_golden, pin_chunking_closed_forms, pin_chunking_rule_invariants, pin_similarity_library,

@@ -19,6 +19,9 @@ DECODE_SRC = os.path.join(ORACLE_DIR, "decode_oracle.py")
 BUDGET_SRC = os.path.join(ORACLE_DIR, "budget_oracle.py")
 
 MUTATIONS = {
+    "layout_no_per_sequence_tiling": ("if cc[sc[b]] != cs[b] or cc[sc[b + 1]] != cs[b + 1]:", "if False:"),
+    "layout_allows_empty_chunk": ("if np.any(np.diff(cc) < 1):", "if np.any(np.diff(cc) < 0):"),
+    "plan_accepts_negative_budget": ("if tk.shape != (C,) or np.any(tk < 0):", "if tk.shape != (C,):"),
     "plain_mean": ("out[c] = mean * np.sqrt(n)", "out[c] = mean"),
     "plain_sum": ("out[c] = mean * np.sqrt(n)", "out[c] = mean * n"),
     "inverse_sqrt": ("out[c] = mean * np.sqrt(n)", "out[c] = mean / np.sqrt(n)"),
