@@ -381,8 +381,8 @@ def chunk_boundaries(cut_bits: torch.Tensor, cu_seqlens, lo: int, hi: int,
                      ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """dhsa_chunk_boundaries: device cu_chunks int32 [T+1] (entries 0..C valid), seq_chunk_start
     int32 [B+1] and num_chunks int32 [1] (``out`` supplies them preallocated)."""
-    if not _on_gpu(cut_bits) or cut_bits.dtype != torch.int64:
-        raise DhsaError(2, "cut_bits", "expected an int64 GPU tensor")
+    if not _on_gpu(cut_bits) or cut_bits.dtype != torch.int64 or not cut_bits.is_contiguous():
+        raise DhsaError(2, "cut_bits", "expected a contiguous int64 tensor on the current GPU")
     sl = _seq_layout(cu_seqlens, cut_bits.device)
     T = sl.total_tokens
     if cut_bits.numel() != (T + 63) // 64:

@@ -19,8 +19,8 @@ template <int D>
 __global__ __launch_bounds__(kRows) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ block_idx,
-    const int32_t* __restrict__ cu_chunks, float* __restrict__ out, float* __restrict__ lse,
-    int C, int T, int Hq, int Hkv, long long nnz, float scale, int row_tiles) {
+    const int32_t* __restrict__ cu_chunks, const int32_t* __restrict__ seq_chunk_start, float* __restrict__ out,
+    float* __restrict__ lse, int B, int C, int T, int Hq, int Hkv, long long nnz, float scale, int row_tiles) {
   __shared__ __attribute__((aligned(16))) float Ks[kKB][D];
   __shared__ __attribute__((aligned(16))) float Vs[kKB][D];
   int bid = blockIdx.x;
@@ -45,9 +45,10 @@ __global__ __launch_bounds__(kRows) void prefill_f32_kernel(
   float m_run = -INFINITY, l_run = 0.f;
 
   const int rp0 = row_ptr[i], rlen = row_ptr[i + 1] - rp0;
+  const int first = seq_chunk_start[seq_of_chunk(seq_chunk_start, B, i)];   // first chunk of i's sequence
   for (int e = 0; e < rlen; ++e) {
     const int j = block_idx[(size_t)h * nnz + rp0 + e];
-    if (j < 0 || j > i) continue;            // only causal chunks of this row are read
+    if (j < first || j > i) continue;        // only chunks of i's sequence up to i are read (-1 padding too)
     const bool diag = j == i;
     const int ks = cu_chunks[j];
     const int ke = diag ? last_row + 1 : cu_chunks[j + 1];
@@ -109,8 +110,8 @@ hipError_t launch_d(const Plan& p, const void* q, const void* k, const void* v, 
   const long long blocks = (long long)p.Hq * p.C * row_tiles;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(prefill_f32_kernel<D>, dim3((unsigned)blocks), dim3(kRows), 0, stream, (const float*)q,
-                     (const float*)k, (const float*)v, row_ptr, block_idx, p.cu_chunks, (float*)out, lse,
-                     p.C, p.T, p.Hq, p.Hkv, (long long)nnz, scale, row_tiles);
+                     (const float*)k, (const float*)v, row_ptr, block_idx, p.cu_chunks, p.seq_chunk_start,
+                     (float*)out, lse, p.B, p.C, p.T, p.Hq, p.Hkv, (long long)nnz, scale, row_tiles);
   return hipGetLastError();
 }
 

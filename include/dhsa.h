@@ -94,7 +94,13 @@ dhsa_status dhsa_validate_layout(const dhsa_layout* layout);
 
 /* Routing plan (host only, pure).  Row i of the compressed block list keeps
  * min(h_topk[i], i_loc) + 1 key chunks, i_loc = i - first chunk of i's
- * sequence: the top-k earlier chunks plus the diagonal.
+ * sequence: the top-k earlier chunks plus the diagonal.  The pages leave the
+ * keep budget open (they say importance decides which token interactions are
+ * kept, not how many: "Long-Context Modeling with Dynamic Hierarchical Sparse
+ * Attention for On-Device LLMs", Abstract); this library makes it an explicit
+ * parameter: a count of earlier chunks per query chunk, the diagonal chunk
+ * always kept on top of it, ties broken toward the lower chunk index (the rule
+ * dhsa_route applies).
  *   h_topk     host [C]   off-diagonal key-chunk budget per query chunk (>= 0)
  *   h_row_ptr  host [C+1] written: CSR row offsets, shared by all q heads
  *   nnz        written: h_row_ptr[C], the entries per q head */
