@@ -22,13 +22,14 @@ DHSA_OK = 0
 DHSA_F32 = 0
 DHSA_BF16 = 1
 STATUS_NAMES = {0: "DHSA_OK", 1: "DHSA_ERR_NULL_ARG", 2: "DHSA_ERR_BAD_SHAPE", 3: "DHSA_ERR_BAD_LAYOUT",
-                4: "DHSA_ERR_BAD_BUDGET", 5: "DHSA_ERR_UNSUPPORTED", 6: "DHSA_ERR_LAUNCH"}
+                4: "DHSA_ERR_BAD_BUDGET", 5: "DHSA_ERR_UNSUPPORTED", 6: "DHSA_ERR_LAUNCH", 7: "DHSA_ERR_WORKSPACE"}
 
 # every entry point declared in include/dhsa.h
 EXPORTS = ("dhsa_abi_version", "dhsa_status_str", "dhsa_validate_layout", "dhsa_route_plan",
            "dhsa_chunk_summarize", "dhsa_route", "dhsa_route_grouped", "dhsa_sparse_prefill",
            "dhsa_adjacent_similarity", "dhsa_chunk_boundaries", "dhsa_decode_workspace_bytes",
-           "dhsa_decode_load_prefix", "dhsa_decode_step", "dhsa_route_plan_tokens", "dhsa_route_tokens")
+           "dhsa_decode_load_prefix", "dhsa_decode_step", "dhsa_route_plan_tokens", "dhsa_route_tokens",
+           "dhsa_decode_step_noalloc")
 
 
 class DhsaError(RuntimeError):
@@ -99,6 +100,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dhsa_decode_step.restype = i32
     lib.dhsa_decode_step.argtypes = [dsp, vp, vp, vp, i32, i32, ctypes.c_float, i32, i32, ctypes.c_float, vp, vp,
                                      vp, ctypes.c_size_t, vp]
+    lib.dhsa_decode_step_noalloc.restype = i32
+    lib.dhsa_decode_step_noalloc.argtypes = [dsp, vp, vp, vp, i32, i32, ctypes.c_float, i32, i32, ctypes.c_float, vp,
+                                             vp, vp]
     if lib.dhsa_abi_version() != 1:
         raise RuntimeError("libdhsa.so ABI version mismatch")
     _LIB = lib
@@ -468,6 +472,19 @@ class DecodeState:
     def step(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lo: int, hi: int, tau: float, topk: int,
              grouped: bool = False, softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
              kept: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """dhsa_decode_step with a workspace this object allocates once per (topk, grouped)."""
+        return self._step(q, k, v, lo, hi, tau, topk, grouped, softmax_scale, out, kept, noalloc=False)
+
+    def step_noalloc(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lo: int, hi: int, tau: float,
+                     topk: int, grouped: bool = False, softmax_scale: Optional[float] = None,
+                     out: torch.Tensor = None, kept: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """dhsa_decode_step_noalloc: the library's static scratch instead of a workspace.  ``out`` is
+        required, so that nothing is allocated on this path either."""
+        if out is None:
+            raise DhsaError(1, "step_noalloc", "out must be given (this path allocates nothing)")
+        return self._step(q, k, v, lo, hi, tau, topk, grouped, softmax_scale, out, kept, noalloc=True)
+
+    def _step(self, q, k, v, lo, hi, tau, topk, grouped, softmax_scale, out, kept, noalloc: bool) -> torch.Tensor:
         self._check_device()
         B = self.seq_len.numel()
         for t, name, heads in ((q, "q", self.num_q_heads), (k, "k", self.num_kv_heads), (v, "v", self.num_kv_heads)):
@@ -478,6 +495,12 @@ class DecodeState:
         _require(kept, "kept", (B, self.num_q_heads, topk), torch.int32)
         if softmax_scale is None:
             softmax_scale = 1.0 / math.sqrt(self.head_dim)
+        if noalloc:
+            _check(load_library().dhsa_decode_step_noalloc(ctypes.byref(self.struct), _ptr(q), _ptr(k), _ptr(v),
+                                                           int(lo), int(hi), float(tau), int(topk), int(grouped),
+                                                           float(softmax_scale), _ptr(out), _ptr(kept), _stream()),
+                   "dhsa_decode_step_noalloc")
+            return out
         if out is None:
             out = torch.empty_like(q)
         ws = self.workspace(topk, grouped)

@@ -212,6 +212,20 @@ dhsa_status plan_tokens(const dhsa_layout* L, const int32_t* h_tb, int32_t* h_ro
   return DHSA_OK;
 }
 
+// Arguments of a decode step other than its scratch (shared by the workspace and static-scratch entries).
+dhsa_status check_decode_step(const dhsa_decode_state* state, const void* q, const void* k, const void* v, int32_t lo,
+                              int32_t hi, float tau, int32_t topk, float softmax_scale, const void* out,
+                              dhsa::DecodeDims* p, dhsa::DecodePtrs* s) {
+  dhsa_status st = check_decode_state(state, p, s);
+  if (st != DHSA_OK) return st;
+  if (lo < 1 || hi < lo || !isfinite(tau)) return DHSA_ERR_BAD_SHAPE;
+  if (topk < 0 || topk >= dhsa::kDecodeMaxChunks) return DHSA_ERR_BAD_BUDGET;
+  if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return DHSA_ERR_BAD_SHAPE;
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return DHSA_ERR_NULL_ARG;
+  if (!all_aligned16(q, k, v, out)) return DHSA_ERR_BAD_SHAPE;
+  return DHSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -227,6 +241,8 @@ const char* dhsa_status_str(int32_t status) {
     case DHSA_ERR_BAD_BUDGET: return "DHSA_ERR_BAD_BUDGET: negative key-chunk budget";
     case DHSA_ERR_UNSUPPORTED: return "DHSA_ERR_UNSUPPORTED: dtype, head_dim or chunk count not supported";
     case DHSA_ERR_LAUNCH: return "DHSA_ERR_LAUNCH: kernel launch failed";
+    case DHSA_ERR_WORKSPACE:
+      return "DHSA_ERR_WORKSPACE: the step needs more scratch than the library's static device array holds";
     default: return "unknown dhsa_status";
   }
 }
@@ -419,16 +435,37 @@ dhsa_status dhsa_decode_step(const dhsa_decode_state* state, const void* q, cons
                              size_t workspace_bytes, void* stream) {
   dhsa::DecodeDims p;
   dhsa::DecodePtrs s;
-  dhsa_status st = check_decode_state(state, &p, &s);
+  dhsa_status st = check_decode_step(state, q, k, v, lo, hi, tau, topk, softmax_scale, out, &p, &s);
   if (st != DHSA_OK) return st;
-  if (lo < 1 || hi < lo || !isfinite(tau)) return DHSA_ERR_BAD_SHAPE;
-  if (topk < 0 || topk >= dhsa::kDecodeMaxChunks) return DHSA_ERR_BAD_BUDGET;
-  if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return DHSA_ERR_BAD_SHAPE;
-  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || workspace == nullptr) return DHSA_ERR_NULL_ARG;
-  if (!all_aligned16(q, k, v, out)) return DHSA_ERR_BAD_SHAPE;
+  if (workspace == nullptr) return DHSA_ERR_NULL_ARG;
   if (((uintptr_t)workspace & 255) != 0) return DHSA_ERR_BAD_SHAPE;
   dhsa::DecodeWork w;
   if (decode_workspace(p, topk, grouped != 0, &w, workspace) > workspace_bytes) return DHSA_ERR_BAD_SHAPE;
+  return launched(dhsa::launch_decode_step(p, s, q, k, v, lo, hi, tau, topk, grouped != 0, softmax_scale, out, kept,
+                                           w, (hipStream_t)stream));
+}
+
+dhsa_status dhsa_decode_step_noalloc(const dhsa_decode_state* state, const void* q, const void* k, const void* v,
+                                     int32_t lo, int32_t hi, float tau, int32_t topk, int32_t grouped,
+                                     float softmax_scale, void* out, int32_t* kept, void* stream) {
+  dhsa::DecodeDims p;
+  dhsa::DecodePtrs s;
+  dhsa_status st = check_decode_step(state, q, k, v, lo, hi, tau, topk, softmax_scale, out, &p, &s);
+  if (st != DHSA_OK) return st;
+  if (decode_workspace(p, topk, grouped != 0, nullptr, nullptr) > dhsa::kNoAllocScratchBytes)
+    return DHSA_ERR_WORKSPACE;
+  // the scratch is the current GPU's copy of the static array, so the stream must belong to that GPU
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return DHSA_ERR_LAUNCH;
+  if (stream != nullptr) {
+    hipDevice_t sd = -1;
+    if (hipStreamGetDevice((hipStream_t)stream, &sd) != hipSuccess) return DHSA_ERR_LAUNCH;
+    if (sd != cur) return DHSA_ERR_UNSUPPORTED;
+  }
+  void* scratch = nullptr;
+  if (dhsa::decode_noalloc_scratch(&scratch) != hipSuccess) return DHSA_ERR_LAUNCH;
+  dhsa::DecodeWork w;
+  decode_workspace(p, topk, grouped != 0, &w, scratch);
   return launched(dhsa::launch_decode_step(p, s, q, k, v, lo, hi, tau, topk, grouped != 0, softmax_scale, out, kept,
                                            w, (hipStream_t)stream));
 }

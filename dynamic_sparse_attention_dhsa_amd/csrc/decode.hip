@@ -27,9 +27,16 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "dhsa_internal.hpp"
 #include "select.hpp"
+
+// Scratch of dhsa_decode_step_noalloc, for callers that cannot allocate device memory.  Every GPU
+// the library runs on holds its own copy of this array from the library's first use there until the
+// process ends.  In host code the name stands for a host-side shadow, not a device address: host code
+// only ever passes the address that dhsa::decode_noalloc_scratch obtains for the current GPU.
+static __device__ __align__(256) uint8_t scratch[dhsa::kNoAllocScratchBytes];
 
 namespace dhsa {
 namespace {
@@ -851,6 +858,25 @@ hipError_t launch_decode_step(const DecodeDims& p, const DecodePtrs& s, const vo
 hipError_t launch_decode_load(const DecodeDims& p, const DecodePtrs& s, const Plan& pl, const void* q, const void* k,
                               const void* v, hipStream_t stream) {
   return p.dtype == 1 ? load_t<uint16_t>(p, s, pl, q, k, v, stream) : load_t<float>(p, s, pl, q, k, v, stream);
+}
+
+hipError_t decode_noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kNoAllocMaxDevices) return hipErrorInvalidDevice;
+  static std::mutex mu;
+  static void* addr[kNoAllocMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {                     // first use on this GPU, which is current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace dhsa

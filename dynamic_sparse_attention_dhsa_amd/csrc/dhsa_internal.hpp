@@ -84,6 +84,13 @@ hipError_t launch_decode_step(const DecodeDims& p, const DecodePtrs& s, const vo
 hipError_t launch_decode_load(const DecodeDims& p, const DecodePtrs& s, const Plan& pl, const void* q, const void* k,
                               const void* v, hipStream_t stream);
 
+// Scratch of the decode step that allocates nothing: a static device array of kNoAllocScratchBytes in
+// decode.hip, one copy per GPU.  Returns the device address of the current GPU's copy (looked up with
+// hipGetSymbolAddress on the first call on that GPU, then cached).
+constexpr size_t kNoAllocScratchBytes = DHSA_NOALLOC_SCRATCH_BYTES;
+constexpr int kNoAllocMaxDevices = 64;
+hipError_t decode_noalloc_scratch(void** ptr);
+
 // Device helpers ----------------------------------------------------------------------------
 
 // Index of the sequence containing chunk c: the last b with seq_chunk_start[b] <= c.

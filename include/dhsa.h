@@ -26,8 +26,9 @@
  *    seq_chunk_start[b] .. seq_chunk_start[b+1]-1 and tile its tokens exactly.
  *  - Pointers without the h_ prefix are HIP device memory; h_ pointers are
  *    host memory.  Everything is OWNED BY THE CALLER: the library allocates
- *    no device memory, keeps no mutable global state, never synchronises, and
- *    enqueues its kernels on `stream` (a hipStream_t; NULL = default stream).
+ *    no device memory, never synchronises, and enqueues its kernels on
+ *    `stream` (a hipStream_t; NULL = default stream).  Its only mutable global
+ *    state is the scratch of dhsa_decode_step_noalloc (see there).
  *  - Errors: every argument, shape and layout problem is detected on the host
  *    (from the h_ mirrors) and returned BEFORE anything is launched; outputs
  *    are then untouched.  A failed launch returns DHSA_ERR_LAUNCH.  The device
@@ -57,7 +58,9 @@ typedef enum dhsa_status {
   DHSA_ERR_BAD_LAYOUT = 3,   /* offsets not monotone, empty chunk, chunk crosses seq */
   DHSA_ERR_BAD_BUDGET = 4,   /* negative top-k                                       */
   DHSA_ERR_UNSUPPORTED = 5,  /* dtype / head_dim / chunk count outside the support   */
-  DHSA_ERR_LAUNCH = 6        /* hipGetLastError after a launch was not hipSuccess    */
+  DHSA_ERR_LAUNCH = 6,       /* hipGetLastError after a launch was not hipSuccess    */
+  DHSA_ERR_WORKSPACE = 7     /* dhsa_decode_step_noalloc: more scratch than the      */
+                             /* library's static device array holds                  */
 } dhsa_status;
 
 typedef enum dhsa_dtype { DHSA_F32 = 0, DHSA_BF16 = 1 } dhsa_dtype;
@@ -308,6 +311,29 @@ dhsa_status dhsa_decode_step(const dhsa_decode_state* state, const void* q, cons
                              int32_t lo, int32_t hi, float tau, int32_t topk, int32_t grouped,
                              float softmax_scale, void* out, int32_t* kept, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* The decode step above for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): same arguments, results and errors as dhsa_decode_step, but the
+ * step's scratch is a static device array inside the library, of
+ * DHSA_NOALLOC_SCRATCH_BYTES, instead of a caller workspace.  Every GPU the
+ * library runs on holds its own copy of that array from the first call there
+ * until the process ends; the call allocates nothing (no hipMalloc, no
+ * allocating library routine) and never synchronises.
+ *   Errors, besides those of dhsa_decode_step: DHSA_ERR_WORKSPACE when this
+ *   state and budget need more scratch than the array holds (the bytes
+ *   dhsa_decode_workspace_bytes reports must not exceed
+ *   DHSA_NOALLOC_SCRATCH_BYTES); DHSA_ERR_UNSUPPORTED when `stream` belongs to
+ *   a GPU other than the current one (the scratch used is the current GPU's).
+ *   Calls on one GPU share its array: calls that may overlap in time (on
+ *   different streams or from different threads) race and must not be made;
+ *   calls in one stream's order are safe.  Nothing in the array needs to start
+ *   at zero: every word a step reads was written earlier in the same step. */
+#define DHSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+dhsa_status dhsa_decode_step_noalloc(const dhsa_decode_state* state, const void* q, const void* k,
+                                     const void* v, int32_t lo, int32_t hi, float tau, int32_t topk,
+                                     int32_t grouped, float softmax_scale, void* out, int32_t* kept,
+                                     void* stream);
 
 #ifdef __cplusplus
 }

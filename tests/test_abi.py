@@ -319,6 +319,44 @@ def test_decode_calls_reject_before_launch():
     assert lib.dhsa_decode_load_prefix(ctypes.byref(state(max_chunks=0)), m.ref(), vp(FAKE), vp(FAKE), vp(FAKE), None) == SHAPE
 
 
+def test_decode_step_noalloc_rejects_before_touching_the_gpu():
+    """dhsa_decode_step_noalloc validates like dhsa_decode_step and refuses a state and budget whose
+    scratch would not fit the library's static array (DHSA_ERR_WORKSPACE), all before any GPU call
+    (the pointers here are fake)."""
+    lib = Bd.load_library()
+    vp = ctypes.c_void_p
+    WORKSPACE = 7
+    assert lib.dhsa_status_str(WORKSPACE).decode().startswith("DHSA_ERR_WORKSPACE")
+    limit = 64 << 20
+
+    def state(**kw):
+        f = dict(num_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=128, dtype=1, max_tokens=4096, max_chunks=256)
+        f.update(kw)
+        return Bd.DecodeStateStruct(f["num_seqs"], f["num_q_heads"], f["num_kv_heads"], f["head_dim"], f["dtype"],
+                                    f["max_tokens"], f["max_chunks"], *([FAKE] * 9))
+
+    def step(st, lo=8, hi=64, tau=0.5, topk=4, grouped=0, scale=0.1, out=FAKE, q=FAKE):
+        return lib.dhsa_decode_step_noalloc(ctypes.byref(st), vp(q), vp(FAKE), vp(FAKE), lo, hi, tau, topk, grouped,
+                                            scale, vp(out) if out else None, None, None)
+
+    good = state()
+    assert step(state(num_q_heads=6, num_kv_heads=4)) == SHAPE
+    assert step(state(head_dim=96)) == UNSUP
+    assert step(state(max_chunks=1025)) == UNSUP
+    assert step(good, lo=0) == SHAPE
+    assert step(good, topk=-1) == BUDGET
+    assert step(good, scale=0.0) == SHAPE
+    assert step(good, out=0) == NULL
+    assert step(good, q=FAKE + 2) == SHAPE
+    # the scratch a step needs is what the workspace query reports; past the limit the call refuses
+    big = state(num_seqs=8, num_q_heads=32, num_kv_heads=8, max_tokens=1 << 17, max_chunks=1024)
+    need = lib.dhsa_decode_workspace_bytes(ctypes.byref(big), 32, 0)
+    assert need > limit
+    assert step(big, topk=32) == WORKSPACE
+    small = state(num_seqs=1, max_tokens=2048, max_chunks=64)
+    assert 0 < lib.dhsa_decode_workspace_bytes(ctypes.byref(small), 4, 1) <= limit
+
+
 def test_misaligned_tensors_are_refused_before_launch():
     """Base pointers of tensors read or written with 16-byte accesses must be 16-byte aligned."""
     lib = Bd.load_library()
