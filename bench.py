@@ -242,46 +242,81 @@ def traffic_record(workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, topk, budget_s: float, grouped: bool = False):
-    """The CPU oracle (as it stands) on a bounded sample of the same workload."""
+_CPU = {}                          # the oracle's inputs, shared with forked workers (copy on write)
+
+
+def _attend_rows(rows):
+    """Oracle attention on (head, chunk) rows in a worker process, BLAS on one thread."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
+    from threadpoolctl import threadpool_limits
+    c = _CPU
+    t0 = time.perf_counter()
+    with threadpool_limits(1):
+        for h, i in rows:
+            oracle.attend(c["q"], c["k"], c["v"], c["cu_chunks"], c["row_ptr"], c["block_idx"], c["scale"],
+                          heads=[h], chunks=[i])
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(w, topk, fraction: float = 0.05, grouped: bool = False, workers: int = 16):
+    """The CPU oracle (as it stands) on a bounded sample of the same workload: summaries and routing of
+    the whole workload on one thread, then oracle attention on random (head, chunk) rows holding at
+    least `fraction` of the kept (query, key) pairs, spread over `workers` processes with one BLAS
+    thread each; the attention time is extrapolated by kept pairs."""
+    import multiprocessing as mp
+
+    import oracle
+    from threadpoolctl import threadpool_limits
+    workers = max(1, min(workers, len(os.sched_getaffinity(0))))
     qf, kf, vf = w.q_f32(), w.k_f32(), w.v_f32()
-    t0 = time.perf_counter()
-    qs = oracle.chunk_summaries(qf, w.cu_chunks)
-    ks = oracle.chunk_summaries(kf, w.cu_chunks)
-    t_sum = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    rp, bi, _ = (oracle.route_grouped if grouped else oracle.route)(qs, ks, w.seq_chunk_start, topk)
-    t_route = time.perf_counter() - t0
-    rng = np.random.default_rng(0)
-    rows = [(int(rng.integers(w.num_q_heads)), int(rng.integers(w.total_chunks))) for _ in range(4096)]
-    lens = np.diff(w.cu_chunks)
-    done_tok = 0
-    t_att = 0.0
-    n_rows = 0
-    for h, i in rows:
+    with threadpool_limits(1):
         t0 = time.perf_counter()
-        oracle.attend(qf, kf, vf, w.cu_chunks, rp, bi, w.softmax_scale, heads=[h], chunks=[i])
-        t_att += time.perf_counter() - t0
-        done_tok += int(lens[i])
-        n_rows += 1
-        if t_att + t_sum + t_route > budget_s:
-            break
-    per_token_head = t_att / done_tok
-    t_att_full = per_token_head * w.total_tokens * w.num_q_heads
+        qs = oracle.chunk_summaries(qf, w.cu_chunks)
+        ks = oracle.chunk_summaries(kf, w.cu_chunks)
+        t_sum = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        rp, bi, _ = (oracle.route_grouped if grouped else oracle.route)(qs, ks, w.seq_chunk_start, topk)
+        t_route = time.perf_counter() - t0
+    lens = np.diff(w.cu_chunks).astype(np.int64)
+    C, Hq = w.total_chunks, w.num_q_heads
+    # kept (query, key) pairs of each row: the causal half of the diagonal plus whole earlier chunks
+    pairs = np.zeros((Hq, C))
+    for h in range(Hq):
+        for i in range(C):
+            kept = bi[h, rp[i]:rp[i + 1]]
+            kept = kept[(kept >= 0) & (kept != i)]
+            pairs[h, i] = lens[i] * lens[kept].sum() + lens[i] * (lens[i] + 1) / 2
+    total = pairs.sum()
+    rng = np.random.default_rng(0)
+    order = rng.permutation(Hq * C)
+    take = np.searchsorted(np.cumsum(pairs.reshape(-1)[order]), fraction * total) + 1
+    rows = [(int(x // C), int(x % C)) for x in order[:take]]
+    sample_pairs = float(sum(pairs[h, i] for h, i in rows))
+    # deal the rows to the workers longest first, so they finish together
+    rows.sort(key=lambda r: -pairs[r])
+    shards = [[] for _ in range(workers)]
+    load = np.zeros(workers)
+    for r in rows:
+        j = int(np.argmin(load))
+        shards[j].append(r)
+        load[j] += pairs[r]
+    _CPU.update(q=qf, k=kf, v=vf, cu_chunks=w.cu_chunks, row_ptr=rp, block_idx=bi, scale=w.softmax_scale)
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(workers) as pool:
+        busy = pool.map(_attend_rows, shards)
+    t_att = time.perf_counter() - t0
+    _CPU.clear()
+    t_att_full = t_att * total / sample_pairs
     t_full = t_sum + t_route + t_att_full
-    return {"value": w.total_tokens / t_full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": (f"oracle summaries + routing of the whole workload ({t_sum + t_route:.1f} s), attention "
-                       f"on {n_rows} random (head, chunk) rows = {done_tok} query-token-heads of "
-                       f"{w.total_tokens * w.num_q_heads} ({t_att:.1f} s), attention time extrapolated per "
-                       f"query-token-head; fp64 numpy"),
+    return {"value": w.total_tokens / t_full, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": (f"oracle summaries + routing of the whole workload on one thread ({t_sum + t_route:.1f} s); "
+                       f"oracle attention on {len(rows)} random (head, chunk) rows holding "
+                       f"{100 * sample_pairs / total:.1f}% of the kept (query, key) pairs, over {workers} worker "
+                       f"processes with one BLAS thread each ({t_att:.1f} s wall), extrapolated by kept pairs; "
+                       f"fp64 numpy"),
             "seconds_est_full_step": t_full, "cpu_model": _cpu_model(),
-            "stage_seconds": {"summaries": t_sum, "routing": t_route, "attention_sample": t_att}}
+            "stage_seconds": {"summaries": t_sum, "routing": t_route, "attention_sample_wall": t_att,
+                              "attention_sample_worker_busy": float(sum(busy))}}
 
 
 def _cpu_model() -> str:
@@ -307,7 +342,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-batch", type=int, default=8,
                     help="sequences in the decode measurement at the workload's context (0: skip it)")
-    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for the baseline")
+    ap.add_argument("--cpu-fraction", type=float, default=0.05,
+                    help="share of the kept (query, key) pairs the oracle baseline computes")
+    ap.add_argument("--cpu-workers", type=int, default=16, help="worker processes of the oracle baseline")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus} GPUs).",
@@ -469,7 +506,7 @@ def main() -> int:
         result["stages"]["stages12_frac_of_read"] = (b1 + b2) / (t1 + t2) / 1e9 / peaks["read_1GiB_GBps"]
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w, w.topk, args.cpu_budget, grouped)
+        result["cpu_baseline"] = cpu_baseline(w, w.topk, args.cpu_fraction, grouped, args.cpu_workers)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -122,7 +122,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // each sequence's pending append record.
 size_t decode_workspace(const dhsa::DecodeDims& p, int topk, bool grouped, dhsa::DecodeWork* w, void* base) {
   const size_t rows = (size_t)p.B * (grouped ? p.Hkv : p.Hq);
-  const int NS = (p.L + dhsa::kDecodeSlice - 1) / dhsa::kDecodeSlice;
+  // one split-K partial state per attention wave of a row: the grid has at most kDecodeGridSlices
+  const int NS = std::min((p.L + dhsa::kDecodeSlice - 1) / dhsa::kDecodeSlice, dhsa::kDecodeGridSlices);
   const size_t o_urow = 0;
   const size_t o_ntok = align256(o_urow + rows * (size_t)p.L * sizeof(int32_t));
   const size_t o_part = align256(o_ntok + rows * sizeof(int32_t));
@@ -152,7 +153,8 @@ dhsa_status check_seqlens(int32_t B, int32_t T, const int32_t* cu_seqlens, const
 // of its sequence whose lengths fit in h_tb[i] (the most any ranking could keep).  A Fenwick tree
 // over chunk lengths (counts and token sums) answers each row in O(log max_len).  Writes
 // h_row_ptr, or (h_row_ptr == nullptr) compares against h_check.  *too_wide: some row with more
-// candidates than the routing registers hold keeps some but not all of them.
+// candidates than the routing registers hold keeps some but not all of them (the general kernel
+// selects those rows).
 dhsa_status plan_tokens(const dhsa_layout* L, const int32_t* h_tb, int32_t* h_row_ptr, const int32_t* h_check,
                         int64_t* nnz, bool* too_wide) {
   const int32_t* sc = L->h_seq_chunk_start;
@@ -219,7 +221,7 @@ dhsa_status check_decode_step(const dhsa_decode_state* state, const void* q, con
   dhsa_status st = check_decode_state(state, p, s);
   if (st != DHSA_OK) return st;
   if (lo < 1 || hi < lo || !isfinite(tau)) return DHSA_ERR_BAD_SHAPE;
-  if (topk < 0 || topk >= dhsa::kDecodeMaxChunks) return DHSA_ERR_BAD_BUDGET;
+  if (topk < 0 || topk >= dhsa::kDecodeMaxTopk) return DHSA_ERR_BAD_BUDGET;
   if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return DHSA_ERR_BAD_SHAPE;
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return DHSA_ERR_NULL_ARG;
   if (!all_aligned16(q, k, v, out)) return DHSA_ERR_BAD_SHAPE;
@@ -333,13 +335,12 @@ dhsa_status dhsa_route_tokens(const dhsa_layout* layout, const float* q_sum, con
   st = plan_tokens(layout, h_token_budget, nullptr, h_row_ptr, &planned, &too_wide);
   if (st != DHSA_OK) return st;
   if (planned != nnz) return DHSA_ERR_BAD_SHAPE;
-  if (too_wide) return DHSA_ERR_UNSUPPORTED;
   if (p.C == 0) return DHSA_OK;
   if (q_sum == nullptr || k_sum == nullptr || token_budget == nullptr || row_ptr == nullptr || block_idx == nullptr)
     return DHSA_ERR_NULL_ARG;
   if (!all_aligned16(q_sum, k_sum)) return DHSA_ERR_BAD_SHAPE;
-  return launched(dhsa::launch_route_tokens(p, q_sum, k_sum, token_budget, row_ptr, nnz, block_idx, grouped != 0,
-                                            (hipStream_t)stream));
+  return launched(dhsa::launch_route_tokens(p, q_sum, k_sum, token_budget, row_ptr, nnz, block_idx, too_wide,
+                                            grouped != 0, (hipStream_t)stream));
 }
 
 dhsa_status dhsa_sparse_prefill(const dhsa_layout* layout, const void* q, const void* k, const void* v,
@@ -407,7 +408,7 @@ dhsa_status dhsa_chunk_boundaries(int32_t num_seqs, int32_t total_tokens, const 
 size_t dhsa_decode_workspace_bytes(const dhsa_decode_state* state, int32_t topk, int32_t grouped) {
   dhsa::DecodeDims p;
   dhsa::DecodePtrs s;
-  if (check_decode_state(state, &p, &s) != DHSA_OK || topk < 0 || topk >= dhsa::kDecodeMaxChunks) return 0;
+  if (check_decode_state(state, &p, &s) != DHSA_OK || topk < 0 || topk >= dhsa::kDecodeMaxTopk) return 0;
   return decode_workspace(p, topk, grouped != 0, nullptr, nullptr);
 }
 

@@ -23,7 +23,7 @@
 // kDecodeSlice kept tokens), or per (sequence, KV group, slice) when routing per
 // KV head, so the group's heads read each K/V row once; QK^T with one token per lane reading its key row, online softmax in base
 // 2, PV with 16-byte value loads, four rows per instruction for d = 128); combine
-// (per (sequence, q head): the slices' partial softmax states).
+// (per (sequence, q head): the attention waves' partial softmax states).
 #include <math.h>
 
 #include <algorithm>
@@ -103,11 +103,87 @@ __device__ inline float row_sum(float x) {
 // cache row and, at a cut, the closed chunk's key summary for head g; every workgroup keeps that
 // summary in LDS and scores it from there; the sequence's counters and running sums are committed by
 // the combine launch (from the pending record the row-0 workgroup leaves).  Then each wave scores a
-// contiguous range of closed chunks into LDS, reading the key summaries across lanes; wave 0 holds
-// the scores in registers, selects the top-k and lays out the row's kept spans (closed chunks
-// ascending, then the open chunk) with their token offsets; every wave writes the spans' cache rows
-// into the row array, and wave 0 the row's total kept tokens.
+// contiguous range of closed chunks into LDS, reading the key summaries across lanes; up to 1024
+// closed chunks, wave 0 holds the scores in registers and selects the top-k, beyond that the whole
+// workgroup selects (block_select); wave 0 lays out the row's kept spans (closed chunks ascending,
+// then the open chunk) with their token offsets, from the chunk table; every wave writes the spans'
+// cache rows into the row array, and wave 0 the row's total kept tokens.
 constexpr int kRouteThreads = 1024;
+constexpr int kRouteWaves = kRouteThreads / 64;
+
+// Top-kk of the n scores in LDS (n up to kDecodeMaxChunks, more than one wave holds in registers) by
+// the whole workgroup, in the rule's order (score desc, chunk asc).  Thread tid owns candidates
+// tid, tid + 1024, ... (their order-preserving bits are re-read from LDS where needed, which keeps
+// the kernel's registers free).  The kk-th best value is found bit by bit from the top with a
+// workgroup count per step (wave ballots, one LDS slot per wave, double-buffered by the step's parity
+// so one barrier a step suffices); then one pass in chunk order keeps those above it and the first
+// ones equal to it.  Writes kl[0 .. kk-1] ascending.  Every thread of the workgroup calls it.
+__device__ inline uint32_t cand_bits(const float* scores, int n, int j) {
+  return j < n ? sel::ordered_bits(scores[j]) : 0u;   // a finite score never maps to 0
+}
+
+__device__ inline int block_total(int (*cnt)[kRouteWaves], int slot, int c, int lane, int wv) {
+  if (lane == 0) cnt[slot][wv] = c;
+  __syncthreads();
+  int tot = 0;
+#pragma unroll 1
+  for (int w = 0; w < kRouteWaves; ++w) tot += cnt[slot][w];
+  return tot;
+}
+
+__device__ inline void block_select(const float* scores, int n, int kk, int32_t* kl, int (*cnt)[kRouteWaves],
+                                    int tid) {
+  const int lane = tid & 63, wv = tid >> 6;
+  const int nb = (n + kRouteThreads - 1) / kRouteThreads;   // batches of 1024 candidates in use
+  uint32_t thr = 0u;
+#pragma unroll 1
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t t = thr | (1u << bit);
+    int c = 0;
+#pragma unroll 1
+    for (int m = 0; m < nb; ++m) c += __popcll(__ballot(cand_bits(scores, n, m * kRouteThreads + tid) >= t));
+    if (block_total(cnt, bit & 1, c, lane, wv) >= kk) thr = t;
+  }
+  int c_above = 0;
+#pragma unroll 1
+  for (int m = 0; m < nb; ++m) c_above += __popcll(__ballot(cand_bits(scores, n, m * kRouteThreads + tid) > thr));
+  // slot 1: the last bit step (bit 0) used slot 0, which slower waves may still be reading
+  const int need = kk - block_total(cnt, 1, c_above, lane, wv);     // equal ones to keep
+  __syncthreads();                               // every wave has read slot 1 before batches reuse it
+  const uint64_t below = (1ull << lane) - 1ull;
+  int eq_base = 0, pos_base = 0;
+#pragma unroll 1
+  for (int m = 0; m < nb; ++m) {
+    const int j = m * kRouteThreads + tid;
+    const uint32_t x = cand_bits(scores, n, j);
+    const bool eq = x == thr;                    // thr >= 1, so only real candidates
+    const uint64_t eqm = __ballot(eq);
+    if (lane == 0) cnt[0][wv] = __popcll(eqm);
+    __syncthreads();
+    int eq_before = eq_base + __popcll(eqm & below), eq_tot = 0;
+#pragma unroll 1
+    for (int w = 0; w < kRouteWaves; ++w) {
+      const int cw = cnt[0][w];
+      eq_before += w < wv ? cw : 0;
+      eq_tot += cw;
+    }
+    const bool keep = x > thr || (eq && eq_before < need);
+    const uint64_t km = __ballot(keep);
+    if (lane == 0) cnt[1][wv] = __popcll(km);
+    __syncthreads();
+    int pos = pos_base + __popcll(km & below), k_tot = 0;
+#pragma unroll 1
+    for (int w = 0; w < kRouteWaves; ++w) {
+      const int cw = cnt[1][w];
+      pos += w < wv ? cw : 0;
+      k_tot += cw;
+    }
+    if (keep) kl[pos] = j;
+    eq_base += eq_tot;
+    pos_base += k_tot;
+    __syncthreads();                             // the counts are rewritten by the next batch
+  }
+}
 
 template <typename T, int D, bool GROUPED>
 __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(
@@ -119,11 +195,11 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(
     int32_t* __restrict__ kept_out, int4* __restrict__ pend) {
   __shared__ __attribute__((aligned(16))) float qv[D];
   __shared__ __attribute__((aligned(16))) float ksn[D];   // key summary of the chunk this token closes
-  __shared__ float red[3][kRouteThreads / 64];
-  __shared__ float scores[sel::kSelCand];
-  __shared__ int32_t kl[sel::kSelCand];
-  __shared__ int3 span_lds[sel::kSelCand + 1];
-  __shared__ int32_t cs_l[sel::kSelCand + 1];    // chunk starts of the sequence, closed chunks then c0
+  __shared__ float red[3][kRouteWaves];
+  __shared__ float scores[kDecodeMaxChunks];
+  __shared__ int32_t kl[kDecodeMaxTopk];          // the kept closed chunks, ascending
+  __shared__ int3 span_lds[kDecodeMaxTopk + 1];
+  __shared__ int sel_cnt[2][kRouteWaves];
   const int R = GROUPED ? Hkv : Hq;
   const int b = blockIdx.x / R, r = blockIdx.x % R, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int G = Hq / Hkv;
@@ -193,8 +269,6 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(
   const float inv = 1.0f / sqrtf((float)(t_end - c0));
   const float* qr = q_run + (size_t)b * Wq;
   const T* qn = q + (size_t)b * Wq;
-  for (int x = tid; x <= nc0; x += kRouteThreads) cs_l[x] = cs[x];  // nc0 <= Cmax <= kDecodeMaxChunks
-  if (cut && tid == 0) cs_l[nc] = c0;
   for (int x = tid; x < D; x += kRouteThreads) {
     float a;
     if constexpr (GROUPED) {
@@ -250,10 +324,12 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(
     }
   }
   __syncthreads();
-  if (tid < 64) {                                 // wave 0 selects
+  // more closed chunks than a wave holds in registers: the workgroup selects (kk, nc block-uniform)
+  if (kk > 0 && kk < nc && nc > sel::kSelCand) block_select(scores, nc, kk, kl, sel_cnt, tid);
+  if (tid < 64) {                                 // wave 0 selects (or finds kl written) and lays out spans
     if (kk == nc) {
       for (int x = lane; x < nc; x += 64) kl[x] = x;
-    } else if (kk > 0) {
+    } else if (kk > 0 && nc <= sel::kSelCand) {
       uint32_t ob[sel::kSelBatches];
       const int nb = (nc + 63) >> 6;
 #pragma unroll
@@ -271,10 +347,10 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(
     for (int base = 0; base <= kk; base += 64) {
       const int i = base + lane;
       int start = 0, len = 0;
-      if (i < kk) {
-        const int j = kl[i];
-        start = cs_l[j];
-        len = cs_l[j + 1] - start;
+      if (i < kk) {                               // closed chunk j: its span from the chunk table;
+        const int j = kl[i];                      // the chunk this token closes (j == nc0) ends at t
+        start = cs[j];
+        len = (j < nc0 ? cs[j + 1] : c0) - start;
       } else if (i == kk) {
         start = c0;
         len = t_end - c0;
@@ -333,7 +409,8 @@ __device__ inline float group_sum(float x) {
 //           normaliser sums the rounded weights;
 //   PV      16-byte value loads, RPV rows per instruction, each lane 8 columns of one row; bf16: two
 //           rows' values repacked into per-column pairs against the two tokens' weights.
-// Partial state per (sequence, q head, slice): (m, l, o[D]), o not normalised.
+// One partial state per (sequence, q head, wave): (m, l, o[D]) over all of the wave's slices, o not
+// normalised.
 template <typename T, int D, bool GROUPED, int GH>
 __global__ __launch_bounds__(64) void decode_attend_kernel(
     const T* __restrict__ q, const T* __restrict__ k_cache, const T* __restrict__ v_cache,
@@ -395,17 +472,18 @@ __global__ __launch_bounds__(64) void decode_attend_kernel(
       for (int e = 0; e < EPL; ++e) qreg[hh][e] = qs[hh][kp * EPL + e];
   }
 
+  // one running softmax state per head across all of this wave's slices (s0, s0 + NSg, ...)
+  float m[GH], l[GH], o[GH][8];
+#pragma unroll
+  for (int hh = 0; hh < GH; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
+  }
   for (int s = s0; s * kDecodeSlice < n; s += NSg) {
     const int lo_tok = s * kDecodeSlice;
     const int hi_tok = min(n, lo_tok + kDecodeSlice);
-    float m[GH], l[GH], o[GH][8];
-#pragma unroll
-    for (int hh = 0; hh < GH; ++hh) {
-      m[hh] = -INFINITY;
-      l[hh] = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
-    }
     // the slice's cache rows (-1 past its end), one load per block
 #pragma unroll
     for (int bk = 0; bk < NB; ++bk) {
@@ -576,26 +654,26 @@ __global__ __launch_bounds__(64) void decode_attend_kernel(
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     }
-    // per head: sum the RPV row groups of each 8-element part
+  }
+  // per head: sum the RPV row groups of each 8-element part; the wave's partial state goes to slot s0
 #pragma unroll
-    for (int hh = 0; hh < GH; ++hh) {
+  for (int hh = 0; hh < GH; ++hh) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ored[lane][e] = o[hh][e];
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      float* dst = part + (((size_t)b * Hq + h0 + hh) * NS + s) * (D + 2);
-      for (int x = lane; x < D; x += 64) {
-        const int p8 = x / 8, e = x % 8;
-        float acc = 0.f;
-        for (int r2 = 0; r2 < RPV; ++r2) acc += ored[r2 * PARTS + p8][e];
-        dst[2 + x] = acc;
-      }
-      if (lane == 0) { dst[0] = m[hh]; dst[1] = l[hh]; }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    for (int e = 0; e < 8; ++e) ored[lane][e] = o[hh][e];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    float* dst = part + (((size_t)b * Hq + h0 + hh) * NS + s0) * (D + 2);
+    for (int x = lane; x < D; x += 64) {
+      const int p8 = x / 8, e = x % 8;
+      float acc = 0.f;
+      for (int r2 = 0; r2 < RPV; ++r2) acc += ored[r2 * PARTS + p8][e];
+      dst[2 + x] = acc;
     }
+    if (lane == 0) { dst[0] = m[hh]; dst[1] = l[hh]; }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   }
 }
 
@@ -605,12 +683,13 @@ __global__ __launch_bounds__(64) void decode_attend_kernel(
 // flight at once.
 template <typename T, int D, bool GROUPED>
 __global__ __launch_bounds__(64) void decode_combine_kernel(
-    const float* __restrict__ part, const int32_t* __restrict__ ntok, int Hq, int Hkv, int NS, T* __restrict__ out,
+    const float* __restrict__ part, const int32_t* __restrict__ ntok, int Hq, int Hkv, int NS, int NSg,
+    T* __restrict__ out,
     const T* __restrict__ q, const T* __restrict__ k, const int4* __restrict__ pend, int Cmax,
     int32_t* __restrict__ seq_len, int32_t* __restrict__ num_closed, int32_t* __restrict__ chunk_start,
     float* __restrict__ q_run, float* __restrict__ k_run, int32_t* __restrict__ status) {
   constexpr int XPL = (D + 63) / 64;              // output columns per lane
-  __shared__ float wgt[kDecodeMaxSlices];
+  __shared__ float wgt[kDecodeGridSlices];
   const int bh = blockIdx.x, lane = threadIdx.x;
   const int b = bh / Hq, h = bh % Hq;
   const int G = Hq / Hkv;
@@ -645,7 +724,8 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
     for (int x = lane; x < D; x += 64) from_f(0.f, op[x]);
     return;
   }
-  const int nsl = (n + kDecodeSlice - 1) / kDecodeSlice;   // <= NS <= kDecodeMaxSlices
+  // partial states: one per attention wave that had a slice (wave s0 took slices s0, s0 + NSg, ...)
+  const int nsl = min((n + kDecodeSlice - 1) / kDecodeSlice, NSg);   // <= NS
   const float* pp = part + (size_t)bh * NS * (D + 2);
   // slice lane in registers; slices past 64 (rows over 64 slices) are read again for their weights
   const float m0 = lane < nsl ? pp[(size_t)lane * (D + 2)] : -INFINITY;
@@ -802,7 +882,8 @@ hipError_t step_d(const DecodeDims& p, const DecodePtrs& s, const void* q, const
 #undef DHSA_ATTEND
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL((decode_combine_kernel<T, D, GROUPED>), dim3(p.B * p.Hq), dim3(64), 0, stream, w.part, w.ntok,
-                     p.Hq, p.Hkv, w.NS, (T*)out, (const T*)q, (const T*)k, (const int4*)w.pend, p.Cmax, s.seq_len,
+                     p.Hq, p.Hkv, w.NS, NSg, (T*)out, (const T*)q, (const T*)k, (const int4*)w.pend, p.Cmax,
+                     s.seq_len,
                      s.num_closed, s.chunk_start, s.q_run, s.k_run, s.status);
   return hipGetLastError();
 }

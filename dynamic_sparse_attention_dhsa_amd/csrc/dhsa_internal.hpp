@@ -33,8 +33,9 @@ hipError_t launch_route(const Plan& p, const float* q_sum, const float* k_sum, c
                         int64_t nnz, int32_t* block_idx, bool wide_rows, bool grouped, hipStream_t stream);
 
 // Stage 2 under a token budget (device token_budget [C]); rows sized by dhsa_route_plan_tokens.
+// `wide_rows`: some row with more candidates than the registers hold keeps some but not all of them.
 hipError_t launch_route_tokens(const Plan& p, const float* q_sum, const float* k_sum, const int32_t* token_budget,
-                               const int32_t* row_ptr, int64_t nnz, int32_t* block_idx, bool grouped,
+                               const int32_t* row_ptr, int64_t nnz, int32_t* block_idx, bool wide_rows, bool grouped,
                                hipStream_t stream);
 
 // Stage 3: block-sparse causal prefill.
@@ -55,8 +56,10 @@ hipError_t launch_chunk_walk(int B, int ntok, const int32_t* cu_seqlens, const u
 
 // Decode (one new token per sequence against the kept structure).
 constexpr int kDecodeSlice = 256;                 // kept tokens per split-K attention workgroup
-constexpr int kDecodeMaxChunks = 1024;            // closed chunks per sequence the routing holds in registers
-constexpr int kDecodeMaxSlices = 4096;            // split-K slices per (sequence, q head): L <= 1M tokens
+constexpr int kDecodeMaxChunks = DHSA_MAX_CHUNKS_PER_SEQ;   // closed chunks per sequence (scores in LDS)
+constexpr int kDecodeMaxTopk = 1024;              // topk < this: the kept list of a row
+constexpr int kDecodeMaxSlices = 4096;            // slices of kept tokens per row: L <= 1M tokens
+constexpr int kDecodeGridSlices = 128;            // attention waves (split-K partial states) per row, at most
 struct DecodeDims {
   int32_t B, Hq, Hkv, d, dtype, L, Cmax;
 };
@@ -74,9 +77,9 @@ struct DecodePtrs {                               // the caller's state (device)
 struct DecodeWork {                               // carved from the caller's workspace
   int32_t* urow;                                  // [B * rows, L]: cache row of each kept token, kept order
   int32_t* ntok;                                  // [B * rows]
-  float* part;                                    // [B * Hq * NS, d + 2]
+  float* part;                                    // [B * Hq * NS, d + 2]: one partial state per attention wave
   int32_t* pend;                                  // [B, 4]: the token's append, committed by the combine
-  int NS;                                         // slices per (sequence, q head)
+  int NS;                                         // partial states per (sequence, q head)
 };
 hipError_t launch_decode_step(const DecodeDims& p, const DecodePtrs& s, const void* q, const void* k, const void* v,
                               int lo, int hi, float tau, int topk, bool grouped, float scale, void* out,

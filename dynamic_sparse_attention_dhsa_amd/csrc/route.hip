@@ -33,7 +33,8 @@
 // pass in chunk order writes those above it plus the first ones equal to it,
 // which is the (score desc, chunk asc) top-k already in ascending chunk order.
 // Rows with more candidates than the registers hold go to a general kernel
-// that bitonic-sorts all of the row's keys in LDS.
+// that bitonic-sorts all of the row's keys in LDS (under a chunk count or a
+// token budget).
 #include "dhsa_internal.hpp"
 #include "select.hpp"
 
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(kWaves * 64) void route_kernel(
       if (lane == 0) out[nc] = i;
       return;
     }
-    if (nc > kRegCand) return;                 // refused on the host: more candidates than registers
+    if (nc > kRegCand) return;                 // more candidates than registers: the general kernel
   } else if (!(kk > 0 && kk < nc && nc <= kRegCand)) {
     if (kk >= nc) {                            // every earlier chunk is kept
       for (int x = lane; x < nc; x += 64) out[x] = first + x;
@@ -194,23 +195,34 @@ __global__ __launch_bounds__(kWaves * 64) void route_kernel(
   }
 }
 
-// General rows: more candidates than the main kernel holds in registers.
-template <int D, bool GROUPED>
+// General rows: more candidates than the main kernel holds in registers.  The row's keys are sorted
+// in LDS (a bitonic network, best first); with a chunk count the first kk are kept, with a token budget
+// (TOKENS) the longest prefix of the sorted order whose chunk lengths fit (a block scan of the lengths
+// in sorted order: the inclusive sums rise strictly, so the kept count is how many stay within the
+// budget).  The kept chunks are written ascending, then the diagonal, then (TOKENS) -1 to the row's end.
+template <int D, bool GROUPED, bool TOKENS>
 __global__ __launch_bounds__(kWideThreads) void route_wide_kernel(
     const float* __restrict__ q_sum, const float* __restrict__ k_sum,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ seq_chunk_start,
-    int32_t* __restrict__ block_idx, int B, int C, int Hq, int Hkv, long long nnz) {
+    int32_t* __restrict__ block_idx, int B, int C, int Hq, int Hkv, long long nnz,
+    const int32_t* __restrict__ cu_chunks, const int32_t* __restrict__ token_budget) {
   __shared__ uint64_t keys[kMaxCand];
   __shared__ uint32_t flags[kMaxCand / 32];
   __shared__ float qrow[D];
   __shared__ int warp_total[kWideThreads / 64];
+  __shared__ int kept_total;
   const int i = blockIdx.x;
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
   const int first = seq_chunk_start[seq_of_chunk(seq_chunk_start, B, i)];
   const int n = i - first;
   const int kk = row_ptr[i + 1] - row_ptr[i] - 1;
-  if (!(kk > 0 && kk < n && n > kRegCand)) return;   // block-uniform
+  if constexpr (TOKENS) {
+    // rows the main kernel writes: few enough candidates, or a budget every earlier chunk fits in
+    if (n <= kRegCand || token_budget[i] >= cu_chunks[i] - cu_chunks[first]) return;   // block-uniform
+  } else {
+    if (!(kk > 0 && kk < n && n > kRegCand)) return;   // block-uniform
+  }
   const int g = h / (Hq / Hkv);
   int npad = 1;
   while (npad < n) npad <<= 1;
@@ -248,14 +260,49 @@ __global__ __launch_bounds__(kWideThreads) void route_wide_kernel(
       __syncthreads();
     }
   }
-  for (int x = tid; x < kk; x += kWideThreads) {
+  const int wave = tid >> 6, lane = tid & 63;
+  int m = kk;                                          // chunks kept before the diagonal
+  if constexpr (TOKENS) {
+    // thread tid takes the consecutive sorted positions [lo, hi): its lengths' sum, a block-wide
+    // exclusive scan of those sums, then its positions whose inclusive sum stays within the budget
+    const int budget = token_budget[i];
+    const int per = (n + kWideThreads - 1) / kWideThreads;
+    const int lo = min(n, tid * per), hi = min(n, lo + per);
+    int seg = 0;
+    for (int x = lo; x < hi; ++x) {
+      const int j = key_chunk(keys[x]);
+      seg += cu_chunks[j + 1] - cu_chunks[j];
+    }
+    int incl = seg;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    if (lane == 63) warp_total[wave] = incl;
+    if (tid == 0) kept_total = 0;
+    __syncthreads();
+    int acc = incl - seg;
+    for (int w = 0; w < wave; ++w) acc += warp_total[w];
+    int cnt = 0;
+    for (int x = lo; x < hi; ++x) {
+      const int j = key_chunk(keys[x]);
+      acc += cu_chunks[j + 1] - cu_chunks[j];
+      if (acc > budget) break;
+      ++cnt;
+    }
+    atomicAdd(&kept_total, cnt);
+    __syncthreads();
+    m = kept_total;
+    __syncthreads();                                   // warp_total is reused below
+  }
+  for (int x = tid; x < m; x += kWideThreads) {
     const int loc = key_chunk(keys[x]) - first;
     atomicOr(&flags[loc >> 5], 1u << (loc & 31));
   }
   __syncthreads();
   // Ascending compaction of the flagged chunks: each wave counts a quarter, then writes.
   int32_t* out = block_idx + (size_t)h * nnz + row_ptr[i];
-  const int wave = tid >> 6, lane = tid & 63;
   const int per = (n + 4 * 64 - 1) / (4 * 64) * 64;
   const int lo = wave * per, hi = min(n, lo + per);
   int cnt = 0;
@@ -276,7 +323,9 @@ __global__ __launch_bounds__(kWideThreads) void route_wide_kernel(
     if (f) out[pos + before] = first + x;
     pos += __popcll(bal);
   }
-  if (tid == 0) out[kk] = i;
+  if (tid == 0) out[m] = i;
+  if constexpr (TOKENS)
+    for (int x = m + 1 + tid; x <= kk; x += kWideThreads) out[x] = -1;   // the row's unused capacity
 }
 
 template <int D, bool GROUPED>
@@ -287,8 +336,9 @@ hipError_t launch_route_d(const Plan& p, const float* q_sum, const float* k_sum,
                      p.seq_chunk_start, block_idx, p.B, p.C, p.Hq, p.Hkv, (long long)nnz, p.cu_chunks, nullptr);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !wide_rows) return err;
-  hipLaunchKernelGGL((route_wide_kernel<D, GROUPED>), dim3(p.C, p.Hq), dim3(kWideThreads), 0, stream, q_sum,
-                     k_sum, row_ptr, p.seq_chunk_start, block_idx, p.B, p.C, p.Hq, p.Hkv, (long long)nnz);
+  hipLaunchKernelGGL((route_wide_kernel<D, GROUPED, false>), dim3(p.C, p.Hq), dim3(kWideThreads), 0, stream, q_sum,
+                     k_sum, row_ptr, p.seq_chunk_start, block_idx, p.B, p.C, p.Hq, p.Hkv, (long long)nnz,
+                     p.cu_chunks, nullptr);
   return hipGetLastError();
 }
 
@@ -299,31 +349,50 @@ hipError_t launch_route_g(const Plan& p, const float* q_sum, const float* k_sum,
                  : launch_route_d<D, false>(p, q_sum, k_sum, row_ptr, nnz, block_idx, wide_rows, stream);
 }
 
-template <int D>
-hipError_t launch_route_tokens_d(const Plan& p, const float* q_sum, const float* k_sum, const int32_t* token_budget,
-                                 const int32_t* row_ptr, int64_t nnz, int32_t* block_idx, bool grouped,
+template <int D, bool GROUPED>
+hipError_t launch_route_tokens_g(const Plan& p, const float* q_sum, const float* k_sum, const int32_t* token_budget,
+                                 const int32_t* row_ptr, int64_t nnz, int32_t* block_idx, bool wide_rows,
                                  hipStream_t stream) {
   dim3 grid(p.C * ((p.Hq + kWaves - 1) / kWaves));
-  if (grouped)
-    hipLaunchKernelGGL((route_kernel<D, true, true>), grid, dim3(kWaves * 64), 0, stream, q_sum, k_sum, row_ptr,
-                       p.seq_chunk_start, block_idx, p.B, p.C, p.Hq, p.Hkv, (long long)nnz, p.cu_chunks, token_budget);
-  else
-    hipLaunchKernelGGL((route_kernel<D, false, true>), grid, dim3(kWaves * 64), 0, stream, q_sum, k_sum, row_ptr,
-                       p.seq_chunk_start, block_idx, p.B, p.C, p.Hq, p.Hkv, (long long)nnz, p.cu_chunks, token_budget);
+  hipLaunchKernelGGL((route_kernel<D, GROUPED, true>), grid, dim3(kWaves * 64), 0, stream, q_sum, k_sum, row_ptr,
+                     p.seq_chunk_start, block_idx, p.B, p.C, p.Hq, p.Hkv, (long long)nnz, p.cu_chunks, token_budget);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || !wide_rows) return err;
+  hipLaunchKernelGGL((route_wide_kernel<D, GROUPED, true>), dim3(p.C, p.Hq), dim3(kWideThreads), 0, stream, q_sum,
+                     k_sum, row_ptr, p.seq_chunk_start, block_idx, p.B, p.C, p.Hq, p.Hkv, (long long)nnz,
+                     p.cu_chunks, token_budget);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_route_tokens_d(const Plan& p, const float* q_sum, const float* k_sum, const int32_t* token_budget,
+                                 const int32_t* row_ptr, int64_t nnz, int32_t* block_idx, bool wide_rows,
+                                 bool grouped, hipStream_t stream) {
+  return grouped ? launch_route_tokens_g<D, true>(p, q_sum, k_sum, token_budget, row_ptr, nnz, block_idx, wide_rows,
+                                                  stream)
+                 : launch_route_tokens_g<D, false>(p, q_sum, k_sum, token_budget, row_ptr, nnz, block_idx, wide_rows,
+                                                   stream);
 }
 
 }  // namespace
 
 hipError_t launch_route_tokens(const Plan& p, const float* q_sum, const float* k_sum, const int32_t* token_budget,
-                               const int32_t* row_ptr, int64_t nnz, int32_t* block_idx, bool grouped,
+                               const int32_t* row_ptr, int64_t nnz, int32_t* block_idx, bool wide_rows, bool grouped,
                                hipStream_t stream) {
   if (p.C == 0) return hipSuccess;
   switch (p.d) {
-    case 32: return launch_route_tokens_d<32>(p, q_sum, k_sum, token_budget, row_ptr, nnz, block_idx, grouped, stream);
-    case 64: return launch_route_tokens_d<64>(p, q_sum, k_sum, token_budget, row_ptr, nnz, block_idx, grouped, stream);
-    case 128: return launch_route_tokens_d<128>(p, q_sum, k_sum, token_budget, row_ptr, nnz, block_idx, grouped, stream);
-    case 256: return launch_route_tokens_d<256>(p, q_sum, k_sum, token_budget, row_ptr, nnz, block_idx, grouped, stream);
+    case 32:
+      return launch_route_tokens_d<32>(p, q_sum, k_sum, token_budget, row_ptr, nnz, block_idx, wide_rows, grouped,
+                                       stream);
+    case 64:
+      return launch_route_tokens_d<64>(p, q_sum, k_sum, token_budget, row_ptr, nnz, block_idx, wide_rows, grouped,
+                                       stream);
+    case 128:
+      return launch_route_tokens_d<128>(p, q_sum, k_sum, token_budget, row_ptr, nnz, block_idx, wide_rows, grouped,
+                                        stream);
+    case 256:
+      return launch_route_tokens_d<256>(p, q_sum, k_sum, token_budget, row_ptr, nnz, block_idx, wide_rows, grouped,
+                                        stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -174,9 +174,7 @@ dhsa_status dhsa_route_plan_tokens(const dhsa_layout* layout, const int32_t* h_t
  *   row_ptr         device [C+1] from dhsa_route_plan_tokens with the same
  *                   budgets; h_row_ptr its host mirror (checked against the plan:
  *                   BAD_SHAPE if it differs, or if nnz does)
- *   block_idx       device [Hq, nnz] int32, written completely
- * UNSUPPORTED when a row with more than 1024 earlier chunks in its sequence
- * keeps some but not all of them. */
+ *   block_idx       device [Hq, nnz] int32, written completely */
 dhsa_status dhsa_route_tokens(const dhsa_layout* layout, const float* q_sum, const float* k_sum,
                               const int32_t* token_budget, const int32_t* h_token_budget,
                               const int32_t* row_ptr, const int32_t* h_row_ptr, int64_t nnz,
@@ -267,7 +265,7 @@ typedef struct dhsa_decode_state {
   int32_t head_dim;          /* d: 64, 128, 256 (bf16) or 64, 128 (fp32)          */
   int32_t dtype;             /* dhsa_dtype of the cache, q, k, v, out             */
   int32_t max_tokens;        /* 1 <= L <= 2^20: cache capacity per sequence       */
-  int32_t max_chunks;        /* C, 1 <= C <= 1024: closed chunks per sequence     */
+  int32_t max_chunks;        /* C, 1 <= C <= 8192: closed chunks per sequence     */
   void* k_cache;             /* [B, L, Hkv, d]                                    */
   void* v_cache;             /* [B, L, Hkv, d]                                    */
   int32_t* seq_len;          /* [B] tokens in the cache                           */
@@ -299,7 +297,8 @@ dhsa_status dhsa_decode_load_prefix(const dhsa_decode_state* state, const dhsa_l
 /* One decode step for every sequence: append token (q [B, Hq, d], k, v [B, Hkv, d]),
  * then write out [B, Hq, d] (its attention output, dtype of the state).
  *   lo, hi, tau     the chunking rule (1 <= lo <= hi, tau finite)
- *   topk            closed chunks kept per row, 0 <= topk <= 1023
+ *   topk            closed chunks kept per row, 0 <= topk <= 1023 (a row may
+ *                   have up to max_chunks closed chunks to choose from)
  *   grouped         0: routing per query head; 1: once per KV head (group-summed
  *                   query summaries, the same kept chunks for the group)
  *   softmax_scale   > 0

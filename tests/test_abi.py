@@ -176,20 +176,18 @@ def test_route_tokens_rejects_before_launch():
                                  None) == BUDGET
     assert lib.dhsa_route_tokens(m.ref(), FAKE, FAKE, FAKE, None, FAKE, rp.ctypes.data, 5, 0, FAKE, None) == NULL
     assert lib.dhsa_route_plan_tokens(m.ref(), tb2.ctypes.data, rp.ctypes.data, ctypes.byref(nnz)) == BUDGET
-    # more than 1024 candidates: only a budget that keeps them all is supported
+    # more than 1024 candidates (selected by the general kernel on the GPU): the plan and the checks
+    # before launch are those of any row
     n = 1100
     cc = np.arange(n + 1, dtype=np.int32)
     w = Mirror([0, n], cc, [0, n])
     rpw = np.zeros(n + 1, np.int32)
-    full = np.arange(n, dtype=np.int32)          # every earlier chunk (length 1) fits
-    assert lib.dhsa_route_plan_tokens(w.ref(), full.ctypes.data, rpw.ctypes.data, ctypes.byref(nnz)) == OK
-    assert lib.dhsa_route_tokens(w.ref(), None, FAKE, FAKE, full.ctypes.data, FAKE, rpw.ctypes.data, nnz.value, 1,
-                                 FAKE, None) == NULL
-    part = full.copy()
-    part[-1] = 5
+    part = np.arange(n, dtype=np.int32)
+    part[-1] = 5                                 # the last row keeps 5 of its 1099 length-1 chunks
     assert lib.dhsa_route_plan_tokens(w.ref(), part.ctypes.data, rpw.ctypes.data, ctypes.byref(nnz)) == OK
-    assert lib.dhsa_route_tokens(w.ref(), FAKE, FAKE, FAKE, part.ctypes.data, FAKE, rpw.ctypes.data, nnz.value, 1,
-                                 FAKE, None) == UNSUP
+    assert rpw[-1] - rpw[-2] == 6
+    assert lib.dhsa_route_tokens(w.ref(), None, FAKE, FAKE, part.ctypes.data, FAKE, rpw.ctypes.data, nnz.value, 1,
+                                 FAKE, None) == NULL
 
 
 def test_stage_calls_reject_before_launch():
@@ -295,11 +293,12 @@ def test_decode_calls_reject_before_launch():
 
     good = state()
     assert lib.dhsa_decode_workspace_bytes(ctypes.byref(good), 4, 0) > 0
-    assert lib.dhsa_decode_workspace_bytes(ctypes.byref(state(max_chunks=2000)), 4, 0) == 0
+    assert lib.dhsa_decode_workspace_bytes(ctypes.byref(state(max_chunks=8193)), 4, 0) == 0
+    assert lib.dhsa_decode_workspace_bytes(ctypes.byref(state(max_chunks=8192)), 4, 0) > 0
     assert step(state(num_q_heads=6, num_kv_heads=4)) == SHAPE
     assert step(state(head_dim=96)) == UNSUP
     assert step(state(dtype=0, head_dim=256)) == UNSUP
-    assert step(state(max_chunks=1025)) == UNSUP
+    assert step(state(max_chunks=8193)) == UNSUP
     assert step(good, lo=0) == SHAPE
     assert step(good, hi=4) == SHAPE
     assert step(good, tau=float("inf")) == SHAPE
@@ -342,7 +341,7 @@ def test_decode_step_noalloc_rejects_before_touching_the_gpu():
     good = state()
     assert step(state(num_q_heads=6, num_kv_heads=4)) == SHAPE
     assert step(state(head_dim=96)) == UNSUP
-    assert step(state(max_chunks=1025)) == UNSUP
+    assert step(state(max_chunks=8193)) == UNSUP
     assert step(good, lo=0) == SHAPE
     assert step(good, topk=-1) == BUDGET
     assert step(good, scale=0.0) == SHAPE

@@ -83,9 +83,9 @@ def _run(seqs, Hq, Hkv, d, dt, seed, P, lo, hi, tau, topk, grouped, L=None, C=25
     return w, outs, kepts, state, status, (qf, kf, vf, scale, P, S, T_seq)
 
 
-def _check(seqs, Hq, Hkv, d, dt, seed, P, lo, hi, tau, topk, grouped=False):
+def _check(seqs, Hq, Hkv, d, dt, seed, P, lo, hi, tau, topk, grouped=False, C=256):
     w, outs, kepts, state, status, (qf, kf, vf, scale, P, S, T_seq) = _run(seqs, Hq, Hkv, d, dt, seed, P, lo, hi,
-                                                                              tau, topk, grouped)
+                                                                              tau, topk, grouped, C=C)
     assert np.all(status == 0)
     cs = w.cu_seqlens
     swaps = 0
@@ -214,6 +214,16 @@ def test_random_decode_settings(i):
 def test_decode_32k_context():
     seqs = [SeqSpec(32768 + 24, ("uniform", 64, 512), 0, 0)]
     _check(seqs, 32, 8, 128, "bf16", 60, 32768, 32, 1024, 0.5, 32, grouped=False)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("grouped", [False, True])
+def test_decode_128k_context_beyond_1024_chunks(grouped):
+    """A 131072-token context in chunks of 24..40 tokens: about 4100 closed chunks, more than one wave
+    holds in registers, so the whole routing workgroup selects the top-k.  Outputs, kept lists and the
+    final chunk table against the decode oracle."""
+    seqs = [SeqSpec(131072 + 12, ("uniform", 24, 40), 0, 0)]
+    _check(seqs, 4, 2, 64, "bf16", 63, 131072, 16, 64, 0.5, 32, grouped=grouped, C=8192)
 
 
 def test_rows_longer_than_the_slice_grid():

@@ -199,17 +199,41 @@ def test_beyond_register_candidates_with_full_rows():
     case.check_attention(heads=[2], chunks=list(range(0, C, 41)))
 
 
-def test_budget_over_register_candidates_is_refused():
+@pytest.mark.parametrize("grouped", [False, True])
+def test_budget_over_register_candidates_takes_the_general_kernel(grouped):
+    """~1250 short chunks in one sequence, budgets that keep some but not all earlier chunks: rows past
+    1024 candidates select in the general kernel (sorted keys, then the longest fitting prefix of the
+    ranking by a block scan of the lengths); every row against the oracle, attention on sampled rows."""
     w = W.make_workload([SeqSpec(6200, ("uniform", 2, 8), 0, 0)], 4, 4, 64, "bf16", seed=38, name="tok_wide")
     C = w.total_chunks
-    budget = np.full(C, 100, np.int32)
-    tdt = torch.bfloat16
-    layout = D.Layout(w.cu_seqlens, w.cu_chunks, w.seq_chunk_start, 4, 4, 64, tdt)
-    plan = D.TokenPlan(layout, budget)
-    qs = torch.zeros((C, 4, 64), dtype=torch.float32, device="cuda")
-    ks = torch.zeros((C, 4, 64), dtype=torch.float32, device="cuda")
-    with pytest.raises(D.DhsaError):
-        D.route_tokens(layout, plan, qs, ks)
+    assert C > 1100
+    rng = np.random.default_rng(10)
+    budget = rng.integers(0, 2000, size=C).astype(np.int32)
+    budget[rng.random(C) < 0.05] = 0
+    case = TokenCase(w, budget, grouped=grouped)
+    first = 0
+    assert any(i - first > 1024 and 0 < budget[i] < w.cu_chunks[i] for i in range(C))
+    case.check_routing()
+    case.check_routing(from_oracle=True)
+    case.check_attention(heads=[1], chunks=list(range(1000, C, 29)))
+    case.check_end_to_end(heads=[0, 3], chunks=[1030, 1100, C - 1])
+
+
+@pytest.mark.slow
+def test_128k_short_chunks_token_budget():
+    """131072 tokens in chunks of 16..48 tokens (about 4100 chunks): most rows have more than 1024
+    candidates and a budget of about 32 mean chunks, so they select in the general kernel; every row's
+    kept list against the oracle, attention on sampled rows."""
+    w = W.make_workload([SeqSpec(131072, ("uniform", 16, 48), 0, 16)], 4, 2, 64, "bf16", seed=44,
+                        name="tok_128k_short")
+    C = w.total_chunks
+    assert C > 3500
+    rng = np.random.default_rng(11)
+    budget = rng.integers(600, 1500, size=C).astype(np.int32)
+    case = TokenCase(w, budget)
+    _, eq, tol = case.check_routing()
+    print(f"[128K short chunks] kept lists: {eq} equal rows, {tol} tolerated", flush=True)
+    case.check_end_to_end(heads=[0, 3], chunks=[0, 1500, 3000, C - 1])
 
 
 @pytest.mark.parametrize("grouped", [False, True])
