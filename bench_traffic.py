@@ -3,7 +3,8 @@
 
 Runs, each as its own rocprofv3 pass (one counter per pass):
   * FETCH_SIZE, then WRITE_SIZE (KiB per dispatch) over ``bench.py`` on the
-    named workload, keeping the prefill kernel's dispatches;
+    named workload (without its decode and CPU-baseline legs), keeping the
+    prefill kernel's dispatches;
   * the same two counters over a plain device copy of known size (a torch
     bf16 tensor copy), which calibrates KiB-as-counted to bytes moved.
 
@@ -83,7 +84,7 @@ def main() -> int:
 
     work = tempfile.mkdtemp(prefix="dhsa_traffic_")
     bench = [sys.executable, "-u", "bench.py", "--config", str(args.config), "--steps", "2", "--warmup", "1",
-             "--no-cpu-baseline"]
+             "--no-cpu-baseline", "--decode-batch", "0"]
     # bench.py's first 1 + 2 prefill launches are the step's (warm-up, then timed); the cold-cache
     # repetitions and the token-budget launches that follow run other lists or other cache states
     step_launches = 3
