@@ -10,11 +10,11 @@
 // Work decomposition.  A workgroup of four waves owns one query chunk i, one
 // KV head g and a tile of query rows; two workgroups share a CU.  Its waves
 // are HP query heads of g (HP = the largest power of two dividing G, at most
-// 4) times 4 / HP blocks of 32 query rows, so one K/V tile staged in LDS feeds
+// 4) times 4 / HP blocks of R query rows, so one K/V tile staged in LDS feeds
 // every q head of the group that keeps it.  The workgroup walks the union of
 // its heads' kept chunks in ascending order (per-head bitmaps in LDS); a
 // head's scores on a chunk it does not keep are masked, and a wave skips the
-// iterations on runs of tiles its head keeps none of.  Key tiles hold 64 keys
+// iterations on runs of tiles its head keeps none of.  Key tiles hold 2R keys
 // in groups of a few rows; a group never crosses a chunk boundary, a tile may
 // (the kept chunks before the diagonal are packed back to back, the diagonal
 // chunk takes tiles of its own); rows past a chunk's end or past the
@@ -32,7 +32,9 @@
 // XCD, where each block's scan over its XCD's groups would grow long, every
 // group is padded to the longest chunk's row tiles instead.)
 //
-// Per tile and wave (32 queries x 64 keys), with v_mfma_f32_32x32x16_bf16:
+// Per tile and wave (R queries x 2R keys), with v_mfma_f32_32x32x16_bf16 (R = 32,
+// head dims 64 and 128) or v_mfma_f32_16x16x32_bf16 (R = 16, head dim 256, where
+// a 32-row wave's O, Q^T and scores would leave room for one wave per SIMD):
 //   S^T = K Q^T      A = K rows from LDS, B = Q^T held in registers for the whole walk
 //   online softmax   base 2, scale*log2(e) folded into one FMA; the running max
 //                    is only moved (and O rescaled) when a tile exceeds it by 2^8
@@ -58,6 +60,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef s16x4 __attribute__((address_space(3))) lds_s16x4;
 typedef void __attribute__((address_space(3))) lds_void;
@@ -75,17 +78,23 @@ constexpr int kSgVALU = 0x002, kSgMFMA = 0x008, kSgDSR = 0x100;
 
 template <int D>
 struct Geo {
+  // Query rows per wave: 32 with 32x32x16 MFMAs; at d = 256 a 32-row wave's O, Q^T and scores would
+  // not fit two waves per SIMD, so there a wave takes 16 rows with 16x16x32 MFMAs and tiles hold 32 keys.
+  static constexpr int ROWS = (D >= 256) ? 16 : 32;
   static constexpr int NW = 4;                           // waves per workgroup (two workgroups per CU)
   static constexpr int NT = NW * 64;
-  static constexpr int BK = 64;                          // keys per tile (two 32-key blocks)
+  static constexpr int BK = 2 * ROWS;                    // keys per tile (two key blocks of ROWS)
   static constexpr int ROWB = 2 * D;                     // bytes per K/V row in LDS (unpadded)
   static constexpr int SLOTS = ROWB / 16;                // 16-byte granules per row
   static constexpr int RPD = 64 / SLOTS;                 // rows per LDS-writing load (64 lanes x 16 B)
   static constexpr int TILEB = BK * ROWB;                // bytes per K (or V) tile
   static constexpr int DPW = TILEB / 1024 / NW;          // LDS-writing loads per wave per tile
-  static constexpr int DSTEPS = D / 16;
-  static constexpr int DBLK = D / 32;
-  static constexpr int MINW = (D >= 256) ? 1 : 2;        // waves per SIMD
+  static constexpr int QK_K = (ROWS == 32) ? 16 : 32;    // head dims per S^T MFMA
+  static constexpr int DSTEPS = D / QK_K;                // S^T MFMAs per key block
+  static constexpr int OB = ROWS;                        // head dims per O^T block (the MFMA's M)
+  static constexpr int DBLK = D / OB;                    // O^T blocks
+  static constexpr int PVK = BK / QK_K;                  // PV MFMAs per O^T block and tile
+  static constexpr int MINW = 2;                         // waves per SIMD
   static_assert(DPW * NW * 1024 == TILEB, "tile must split evenly over the waves");
   // Granule swizzles (physical slot = logical granule ^ swizzle(row)) for 64 four-byte banks:
   //  K: the 16 lanes of a 16-byte fragment read take 16 consecutive rows at one logical granule;
@@ -93,7 +102,11 @@ struct Geo {
   // Both are XOR-linear in the row bits they use, so the swizzle of row 32b + r, 16k + r, 8k + r or
   // RPD * m + r splits into a per-lane part and a constant.
   static constexpr __host__ __device__ int kswz(int r) { return D >= 128 ? (r & 15) : ((r >> 1) & 7); }
-  static constexpr __host__ __device__ int vswz(int r) { return D >= 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+  //  V with 16-row waves: the four 16-lane groups of a transpose read take rows 4g .. 4g + 3 of one
+  //  column range; row bit 2 moves groups g and g + 1 (read in the same cycle) to other banks.
+  static constexpr __host__ __device__ int vswz(int r) {
+    return ROWS == 16 ? (4 * (r & 3)) ^ (2 * ((r >> 2) & 1)) : (D >= 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1));
+  }
 };
 
 // Lowest set bit index >= x of the bitmap bu (nbits bits), or -1.
@@ -117,6 +130,15 @@ __device__ inline float max_halves(float x) {
 }
 __device__ inline float sum_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// the same over lanes l and l ^ 16 (16-lane rows swapped in pairs)
+__device__ inline float max_rows16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_rows16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
@@ -149,7 +171,8 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
   // ---- block -> (KV head, chunk, head slot, row tile); group g = (KV head, chunk) on XCD g % 8
   const int G = Hq / Hkv;
   const int rb_count = NW / hp;
-  const int rows_blk = rb_count * 32;
+  constexpr int ROWS = GE::ROWS;
+  const int rows_blk = rb_count * ROWS;
   const int xcd = blockIdx.x & 7;
   const int kth = blockIdx.x >> 3;                         // position among this XCD's blocks
   const int ngroups = Hkv * C;
@@ -213,12 +236,12 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hw = wave % hp;
   const int h = gk * G + hs * hp + hw;
-  const int qr0 = q0 + (wave / hp) * 32;
+  const int qr0 = q0 + (wave / hp) * ROWS;
   const bool wave_rows = qr0 < e_i;
   const int first = __builtin_amdgcn_readfirstlane(seq_chunk_start[seq_of_chunk(seq_chunk_start, B, i)]);
   const int nbits = i - first + 1;
   const int rp0 = row_ptr[i], rlen = row_ptr[i + 1] - rp0;
-  const int diag_end = min(e_i, q0 + rb_count * 32);
+  const int diag_end = min(e_i, q0 + rb_count * ROWS);
 
   // ---- kept-chunk bitmaps of the workgroup's heads
   const int nwords = (nbits + 31) >> 5;
@@ -236,7 +259,9 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
   __syncthreads();
 
   // ---- Q^T fragments (B operand), whole walk
-  const int col = lane & 31, half = lane >> 5;
+  // a lane's query column, and which slice of the MFMA's k (or of the accumulator's rows) it holds:
+  // 0..1 with 32-row waves, 0..3 with 16-row waves
+  const int col = lane & (ROWS - 1), half = lane / ROWS;
   const int tq = qr0 + col;
   bf16x8 qf[GE::DSTEPS];
   {
@@ -244,7 +269,7 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
     const uint16_t* qp = q + ((size_t)tq * Hq + h) * D + half * 8;
 #pragma unroll
     for (int s = 0; s < GE::DSTEPS; ++s) {
-      uint4 raw = ok ? *reinterpret_cast<const uint4*>(qp + s * 16) : make_uint4(0, 0, 0, 0);
+      uint4 raw = ok ? *reinterpret_cast<const uint4*>(qp + s * GE::QK_K) : make_uint4(0, 0, 0, 0);
       qf[s] = __builtin_bit_cast(bf16x8, raw);
     }
   }
@@ -359,93 +384,132 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
   };
 
   // ---- per-lane LDS read offsets (bytes)
-  // K fragment of S^T = K Q^T: row col (+32 for the second key block), logical granule 2s + half at
-  // step s; physical byte (col * ROWB + 16 * (half ^ kswz(col))) ^ 32 s
+  // K fragment of S^T = K Q^T: key row col of the block (col + ROWS for the second one), logical
+  // granule (QK_K / 8) st + half at step st; physical byte (col * ROWB + 16 * (half ^ kswz(col))) ^ 2 QK_K st
   const int k_lane = col * GE::ROWB + 16 * (half ^ GE::kswz(col));
-  // V^T fragment, transpose load: the 16-lane group grp reads key rows 4 (grp / 2) + ii / 4 (+8 for the
+  // V^T fragment, transpose load (a 16-lane group reads 4 rows x 16 columns and each lane receives one
+  // column of the 4 rows).  32-row waves: the group grp reads key rows 4 (grp / 2) + ii / 4 (+8 for the
   // upper half, +16 per k-step), dims 16 (grp % 2) + 4 (ii % 4) of the 32-dim block db; physical byte
-  // v_lane ^ 64 db
+  // v_lane ^ 64 db.  16-row waves: group grp reads key rows 4 grp + ii / 4 (+16 for the upper half),
+  // dims 4 (ii % 4) of the 16-dim block db; physical byte v_lane ^ 32 db.
   const int grp = (lane >> 4) & 3, ii = lane & 15;
-  const int vrow = 4 * (grp >> 1) + (ii >> 2);
-  const int v_lane = vrow * GE::ROWB + 16 * ((2 * (grp & 1) + ((ii & 3) >> 1)) ^ GE::vswz(vrow)) + 8 * (ii & 1);
+  int v_lane;
+  if constexpr (ROWS == 32) {
+    const int vrow = 4 * (grp >> 1) + (ii >> 2);
+    v_lane = vrow * GE::ROWB + 16 * ((2 * (grp & 1) + ((ii & 3) >> 1)) ^ GE::vswz(vrow)) + 8 * (ii & 1);
+  } else {
+    const int vrow = 4 * grp + (ii >> 2);
+    v_lane = vrow * GE::ROWB + 16 * (((ii & 3) >> 1) ^ GE::vswz(vrow)) + 8 * (ii & 1);
+  }
+  constexpr int VHI = (ROWS == 32) ? 8 : 16;               // rows between a transpose read's two halves
+  constexpr int VDB = (ROWS == 32) ? 64 : 32;              // byte XOR per O^T block
 
-  f32x16 o[GE::DBLK];
+  // accumulators: S^T of a tile as two ROWS x ROWS key blocks, O^T as DBLK blocks of OB dims
+  using Acc = std::conditional_t<ROWS == 32, f32x16, f32x4>;
+  constexpr int NA = (ROWS == 32) ? 16 : 4;                // accumulator registers per block
+  constexpr int NPW = BK * ROWS / 128;                     // packed bf16 weight pairs per lane and tile
+  Acc o[GE::DBLK];
 #pragma unroll
   for (int db = 0; db < GE::DBLK; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+    for (int r = 0; r < NA; ++r) o[db][r] = 0.f;
   // lb_run: sum of the bf16 weights actually multiplied into V, which normalises O (a dominant
   // weight cancels exactly); l_run: sum of the fp32 weights, kept only when the LSE is wanted
   float m_ref = -INFINITY, l_run = 0.f, lb_run = 0.f;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   const float c2 = scale * kLog2e;
   const float grow_raw = kRescaleLog2 / c2;
-  const f32x16 zero16 = {};
+  const Acc zeroA = {};
+  auto mfma = [](const bf16x8& a, const bf16x8& b, const Acc& c) __attribute__((always_inline)) {
+    if constexpr (ROWS == 32) return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    else return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  };
+  // reductions over the lanes holding one query column: l ^ 32 (32-row waves), l ^ 16 and l ^ 32 (16-row)
+  auto col_max = [](float x) __attribute__((always_inline)) {
+    if constexpr (ROWS == 16) x = max_rows16(x);
+    return max_halves(x);
+  };
+  auto col_sum = [](float x) __attribute__((always_inline)) {
+    if constexpr (ROWS == 16) x = sum_rows16(x);
+    return sum_halves(x);
+  };
 
-  // S^T[b][r] holds tile row 32b + 8(r/4) + 4*half + r%4 of query `col`.
+  // 32-row waves: S^T[b][r] holds tile row 32b + 8(r/4) + 4*half + r%4 of query `col`.
+  // 16-row waves: S^T[b][r] holds tile row 16b + 4*half + r of query `col`.
   // A tile needs masking when a group has fewer real, kept rows than GS, or when it is a tile of the
   // diagonal chunk with a key past the wave's first query row.
   auto needs_mask = [&](const TileRef& t) __attribute__((always_inline)) {
     return t.nval != kFull || (t.kt >= 0 && t.kt + BK - 1 > qr0);
   };
-  auto apply_mask = [&](f32x16 (&s)[2], const TileRef& t) __attribute__((always_inline)) {
-    // rows past lim (in the lane's frame, which starts at row 4 * half) fail the causal test
-    const int lim = (t.kt >= 0 ? tq - t.kt : BK) - 4 * half;
+  auto apply_mask = [&](Acc (&s)[2], const TileRef& t) __attribute__((always_inline)) {
     const uint64_t nv = t.nval;
-    const int hs4 = 4 * half;
+    if constexpr (ROWS == 32) {
+      // rows past lim (in the lane's frame, which starts at row 4 * half) fail the causal test
+      const int lim = (t.kt >= 0 ? tq - t.kt : BK) - 4 * half;
+      const int hs4 = 4 * half;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int base = 32 * b + 8 * q4;    // lane-frame row of r = 4 q4 (plus 4 * half for the tile row)
-        if constexpr (GS == 4) {             // group 8b + 2q4 + half, row in group r % 4
-          const int n = (int)((nv >> (NB * (8 * b + 2 * q4) + NB * half)) & 0xF);
-          const int nn = min(n, lim - base + 1);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int base = 32 * b + 8 * q4;  // lane-frame row of r = 4 q4 (plus 4 * half for the tile row)
+          if constexpr (GS == 4) {           // group 8b + 2q4 + half, row in group r % 4
+            const int n = (int)((nv >> (NB * (8 * b + 2 * q4) + NB * half)) & 0xF);
+            const int nn = min(n, lim - base + 1);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) s[b][4 * q4 + e] = (e < nn) ? s[b][4 * q4 + e] : -INFINITY;
-        } else if constexpr (GS == 8) {      // group 4b + q4, row in group 4 * half + r % 4
-          const int n = (int)((nv >> (NB * (4 * b + q4))) & 0xFF) - hs4;
-          const int nn = min(n, lim - base + 1);
+            for (int e = 0; e < 4; ++e) s[b][4 * q4 + e] = (e < nn) ? s[b][4 * q4 + e] : -INFINITY;
+          } else {                           // GS == 8: group 4b + q4, row in group 4 * half + r % 4
+            const int n = (int)((nv >> (NB * (4 * b + q4))) & 0xFF) - hs4;
+            const int nn = min(n, lim - base + 1);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) s[b][4 * q4 + e] = (e < nn) ? s[b][4 * q4 + e] : -INFINITY;
-        } else {                             // GS == 2: group 16b + 4q4 + 2half + e/2, row in group e % 2
-#pragma unroll
-          for (int p2 = 0; p2 < 2; ++p2) {
-            const int n = (int)((nv >> (NB * (16 * b + 4 * q4 + p2) + 2 * NB * half)) & 0x3);
-            const int nn = min(n, lim - base - 2 * p2 + 1);
-#pragma unroll
-            for (int e = 0; e < 2; ++e)
-              s[b][4 * q4 + 2 * p2 + e] = (e < nn) ? s[b][4 * q4 + 2 * p2 + e] : -INFINITY;
+            for (int e = 0; e < 4; ++e) s[b][4 * q4 + e] = (e < nn) ? s[b][4 * q4 + e] : -INFINITY;
           }
         }
-      }
+    } else {
+      // GS == 2: register r of block b is tile row 16b + 4 half + r, group 8b + 2 half + r / 2
+      const int lim = (t.kt >= 0 ? tq - t.kt : BK) - 4 * half;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int p2 = 0; p2 < 2; ++p2) {
+          const int n = (int)((nv >> (NB * (8 * b + p2) + 2 * NB * half)) & 0x3);
+          const int nn = min(n, lim - 16 * b - 2 * p2 + 1);
+#pragma unroll
+          for (int e = 0; e < 2; ++e) s[b][2 * p2 + e] = (e < nn) ? s[b][2 * p2 + e] : -INFINITY;
+        }
+    }
   };
 
   // QK^T of the next tile (if QN) interleaved with the softmax of the current tile (if SM).
   // Leaves P^T of the current tile packed in pw and the running max / sums updated; returns alpha.
-  uint32_t pw[16];
-  auto region_a = [&](auto qn_c, auto sm_c, const uint8_t* kst, f32x16 (&sn)[2], f32x16 (&sc)[2],
+  uint32_t pw[NPW];
+  auto region_a = [&](auto qn_c, auto sm_c, const uint8_t* kst, Acc (&sn)[2], Acc (&sc)[2],
                       float& alpha) __attribute__((always_inline)) {
     constexpr bool QN = decltype(qn_c)::value, SM = decltype(sm_c)::value;
     if constexpr (QN) {
       const uint8_t* kb = kst + 0;
 #pragma unroll
       for (int st = 0; st < GE::DSTEPS; ++st) {
-        const int ko = k_lane ^ (32 * st);
+        const int ko = k_lane ^ (2 * GE::QK_K * st);
         const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kb + ko);
-        sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[st], st == 0 ? zero16 : sn[0], 0, 0, 0);
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kb + 32 * GE::ROWB + ko);
-        sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[st], st == 0 ? zero16 : sn[1], 0, 0, 0);
+        sn[0] = mfma(a0, qf[st], st == 0 ? zeroA : sn[0]);
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kb + ROWS * GE::ROWB + ko);
+        sn[1] = mfma(a1, qf[st], st == 0 ? zeroA : sn[1]);
       }
     }
     if constexpr (SM) {
       // reductions as shallow trees (four independent partial results) to keep dependency chains short
-      float m4[4];
+      float mx;
+      if constexpr (ROWS == 32) {
+        float m4[4];
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
-        m4[x] = fmaxf(fmaxf(fmaxf(sc[0][x], sc[0][x + 4]), fmaxf(sc[0][x + 8], sc[0][x + 12])),
-                      fmaxf(fmaxf(sc[1][x], sc[1][x + 4]), fmaxf(sc[1][x + 8], sc[1][x + 12])));
-      const float mx = max_halves(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+        for (int x = 0; x < 4; ++x)
+          m4[x] = fmaxf(fmaxf(fmaxf(sc[0][x], sc[0][x + 4]), fmaxf(sc[0][x + 8], sc[0][x + 12])),
+                        fmaxf(fmaxf(sc[1][x], sc[1][x + 4]), fmaxf(sc[1][x + 8], sc[1][x + 12])));
+        mx = col_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+      } else {
+        mx = col_max(fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                           fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3]))));
+      }
       const bool grow = mx > m_ref + grow_raw;
       const float m_new = grow ? mx : m_ref;
       alpha = grow ? __builtin_amdgcn_exp2f((m_ref - m_new) * c2) : 1.f;   // 0 at the first tile
@@ -454,34 +518,35 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[b][r] = __builtin_amdgcn_exp2f(fmaf(sc[b][r], c2, -mb));
+        for (int r = 0; r < NA; ++r) sc[b][r] = __builtin_amdgcn_exp2f(fmaf(sc[b][r], c2, -mb));
       float lb4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          pw[b * 8 + r / 2] = pack_bf16(sc[b][r], sc[b][r + 1]);
-          lb4[(r / 2) & 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[b * 8 + r / 2]), ones,
-                                                             lb4[(r / 2) & 3], false);
+        for (int r = 0; r < NA; r += 2) {
+          const int x = b * (NA / 2) + r / 2;
+          pw[x] = pack_bf16(sc[b][r], sc[b][r + 1]);
+          lb4[x & 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[x]), ones, lb4[x & 3], false);
         }
-      lb_run = lb_run * alpha + sum_halves((lb4[0] + lb4[1]) + (lb4[2] + lb4[3]));
+      lb_run = lb_run * alpha + col_sum((lb4[0] + lb4[1]) + (lb4[2] + lb4[3]));
       if constexpr (WITH_LSE) {
         float ls4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) ls4[r & 3] += sc[b][r];
-        l_run = l_run * alpha + sum_halves((ls4[0] + ls4[1]) + (ls4[2] + ls4[3]));
+          for (int r = 0; r < NA; ++r) ls4[r & 3] += sc[b][r];
+        l_run = l_run * alpha + col_sum((ls4[0] + ls4[1]) + (ls4[2] + ls4[3]));
       }
     }
     // interleave: each QK MFMA followed by its next K read and a slice of the softmax
     if constexpr (QN && SM) {
+      constexpr int SMV = (ROWS == 32) ? 120 : 48;          // softmax VALU instructions, about
       __builtin_amdgcn_sched_group_barrier(kSgDSR, 4, 0);
 #pragma unroll
       for (int x = 0; x < 2 * GE::DSTEPS; ++x) {
         __builtin_amdgcn_sched_group_barrier(kSgMFMA, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSgDSR, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgVALU, 120 / (2 * GE::DSTEPS) + 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgVALU, SMV / (2 * GE::DSTEPS) + 1, 0);
       }
     }
   };
@@ -489,22 +554,22 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
   // O^T += V^T P^T for the current tile
   auto region_b = [&](const uint8_t* vst) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < GE::PVK; ++ks) {
       const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pw[ks * 4], pw[ks * 4 + 1], pw[ks * 4 + 2],
                                                               pw[ks * 4 + 3]));
 #pragma unroll
       for (int db = 0; db < GE::DBLK; ++db) {
-        const uint8_t* p0 = vst + (v_lane ^ (64 * db)) + ks * 16 * GE::ROWB;
+        const uint8_t* p0 = vst + (v_lane ^ (VDB * db)) + ks * 16 * GE::ROWB;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * GE::ROWB));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + VHI * GE::ROWB));
         const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
         const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf, o[db], 0, 0, 0);
+        o[db] = mfma(a, pf, o[db]);
       }
     }
     __builtin_amdgcn_sched_group_barrier(kSgDSR, 6, 0);
 #pragma unroll
-    for (int x = 0; x < 4 * GE::DBLK; ++x) {
+    for (int x = 0; x < GE::PVK * GE::DBLK; ++x) {
       __builtin_amdgcn_sched_group_barrier(kSgMFMA, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSgDSR, 2, 0);
     }
@@ -522,7 +587,7 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
   // Waves without query rows (possible when the workgroup holds several row blocks) only stage
   // tiles.  Every other wave runs the same straight-line tile body: after the last tile the QK^T of
   // the (absent) next tile reads a stale but finite K stage and is discarded.
-  f32x16 sA[2], sB[2] = {zero16, zero16};      // sB is first read after a skipped iteration
+  Acc sA[2], sB[2] = {zeroA, zeroA};           // sB is first read after a skipped iteration
   if (wave_rows) {
     float dummy;
     region_a(std::true_type{}, std::false_type{}, k_st0, sA, sB, dummy);   // S^T of tile 0
@@ -531,7 +596,7 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
 
   // One iteration with stage parity S: softmax and PV of t0 (S^T in sc, V in V stage S), QK^T of t1
   // (K in K stage 1 - S, into sn); meanwhile K of t2 lands in K stage S and V of t1 in V stage 1 - S.
-  auto step = [&](auto s_c, f32x16 (&sc)[2], f32x16 (&sn)[2]) __attribute__((always_inline)) {
+  auto step = [&](auto s_c, Acc (&sc)[2], Acc (&sn)[2]) __attribute__((always_inline)) {
     constexpr int S = decltype(s_c)::value;
     uint8_t* const k_fill = S ? k_st1 : k_st0;
     uint8_t* const k_read = S ? k_st0 : k_st1;
@@ -557,7 +622,7 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
 #pragma unroll
         for (int db = 0; db < GE::DBLK; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+          for (int r = 0; r < NA; ++r) o[db][r] *= alpha;
       }
       region_b(v_read);
     }
@@ -575,14 +640,16 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
   if (!wave_rows || tq >= e_i) return;
   const float inv_l = 1.0f / lb_run;
   uint16_t* op = out + ((size_t)tq * Hq + h) * D;
+  // O^T block db, accumulator register r: head dim OB db + (32-row waves) 8 (r / 4) + 4 half + r % 4,
+  // (16-row waves) 4 half + r
 #pragma unroll
   for (int db = 0; db < GE::DBLK; ++db) {
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
+    for (int g4 = 0; g4 < NA / 4; ++g4) {
       uint2 w;
       w.x = pack_bf16(o[db][g4 * 4 + 0] * inv_l, o[db][g4 * 4 + 1] * inv_l);
       w.y = pack_bf16(o[db][g4 * 4 + 2] * inv_l, o[db][g4 * 4 + 3] * inv_l);
-      *reinterpret_cast<uint2*>(op + db * 32 + 8 * g4 + 4 * half) = w;
+      *reinterpret_cast<uint2*>(op + db * GE::OB + 8 * g4 + 4 * half) = w;
     }
   }
   if constexpr (WITH_LSE) {
@@ -598,7 +665,7 @@ hipError_t launch_d(const Plan& p, const void* q, const void* k, const void* v, 
   const int G = p.Hq / p.Hkv;
   int hp = 1;
   while (hp < GE::NW && G % (hp * 2) == 0) hp *= 2;
-  const int rows_per_block = (GE::NW / hp) * 32;
+  const int rows_per_block = (GE::NW / hp) * GE::ROWS;
   const int row_tiles = (p.max_chunk_len + rows_per_block - 1) / rows_per_block;
   const int head_slots = G / hp;
   const long long groups = (long long)p.Hkv * p.C;
