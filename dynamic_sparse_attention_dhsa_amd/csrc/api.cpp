@@ -101,7 +101,7 @@ dhsa_status check_decode_state(const dhsa_decode_state* st, dhsa::DecodeDims* di
     return DHSA_ERR_UNSUPPORTED;
   }
   if (st->max_chunks > dhsa::kDecodeMaxChunks) return DHSA_ERR_UNSUPPORTED;
-  if ((st->max_tokens + dhsa::kDecodeSlice - 1) / dhsa::kDecodeSlice > dhsa::kDecodeMaxSlices) return DHSA_ERR_UNSUPPORTED;
+  if (st->max_tokens > dhsa::kDecodeMaxTokens) return DHSA_ERR_UNSUPPORTED;
   const int64_t elem = st->dtype == DHSA_BF16 ? 2 : 4;
   if ((int64_t)st->max_tokens * st->num_kv_heads * st->head_dim * elem > ((int64_t)1 << 40)) return DHSA_ERR_UNSUPPORTED;
   if (st->k_cache == nullptr || st->v_cache == nullptr || st->seq_len == nullptr || st->num_closed == nullptr ||
@@ -127,7 +127,7 @@ size_t decode_workspace(const dhsa::DecodeDims& p, int topk, bool grouped, dhsa:
   const size_t o_urow = 0;
   const size_t o_ntok = align256(o_urow + rows * (size_t)p.L * sizeof(int32_t));
   const size_t o_part = align256(o_ntok + rows * sizeof(int32_t));
-  const size_t o_pend = align256(o_part + (size_t)p.B * p.Hq * NS * (p.d + 2) * sizeof(float));
+  const size_t o_pend = align256(o_part + (size_t)p.B * p.Hq * NS * (p.d + dhsa::kPartHead) * sizeof(float));
   const size_t total = align256(o_pend + (size_t)p.B * 4 * sizeof(int32_t));
   if (w != nullptr) {
     char* c = (char*)base;

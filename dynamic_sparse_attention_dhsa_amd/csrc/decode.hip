@@ -15,15 +15,20 @@
 //   * attention: exact softmax of the token's query over the tokens of the kept
 //     closed chunks and of the open chunk up to t.
 //
-// Kernels, in stream order: append (one workgroup per sequence: similarity with
-// the previous key row by a block reduction, the cut, the running sums, the
-// cache rows); route (one wave per (sequence, row): scores of up to 1024 closed
-// chunks in registers, the shared radix top-k, then the kept spans with their
-// token offsets); attend (split-K: one wave per (sequence, q head, slice of
-// kDecodeSlice kept tokens), or per (sequence, KV group, slice) when routing per
-// KV head, so the group's heads read each K/V row once; QK^T with one token per lane reading its key row, online softmax in base
-// 2, PV with 16-byte value loads, four rows per instruction for d = 128); combine
-// (per (sequence, q head): the attention waves' partial softmax states).
+// Kernels, in stream order: route (one 1024-thread workgroup per (sequence,
+// row), a row being a q head or, routed per KV head, a KV head: every workgroup
+// takes the append decision from the pre-token state (similarity with the
+// previous key row by a block reduction, the cut); the KV head's owner writes
+// the cache row and the closing chunk's key summary; scores of the closed
+// chunks in LDS, the radix top-k in registers up to 1024 candidates and an
+// LDS selection beyond, then the kept spans' cache rows); attend (split-K: one
+// wave per (sequence, q head, slices of kDecodeSlice kept tokens), or per
+// (sequence, KV group, slices) when routing per KV head, so the group's heads
+// read each K/V row once; key rows read across lanes with the partial dot
+// products summed on the DPP paths, online softmax in base 2 with one token per
+// lane, PV with 16-byte value loads); combine (per (sequence, q head): the
+// attention waves' partial softmax states, then the append's counters and
+// running sums are committed).
 #include <math.h>
 
 #include <algorithm>
@@ -409,8 +414,8 @@ __device__ inline float group_sum(float x) {
 //           normaliser sums the rounded weights;
 //   PV      16-byte value loads, RPV rows per instruction, each lane 8 columns of one row; bf16: two
 //           rows' values repacked into per-column pairs against the two tokens' weights.
-// One partial state per (sequence, q head, wave): (m, l, o[D]) over all of the wave's slices, o not
-// normalised.
+// One partial state per (sequence, q head, wave): (m, l, two unused floats, o[D]) over all of the
+// wave's slices, o not normalised (o starts 16 bytes into the row, so it is read with 16-byte loads).
 template <typename T, int D, bool GROUPED, int GH>
 __global__ __launch_bounds__(64) void decode_attend_kernel(
     const T* __restrict__ q, const T* __restrict__ k_cache, const T* __restrict__ v_cache,
@@ -663,12 +668,12 @@ __global__ __launch_bounds__(64) void decode_attend_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    float* dst = part + (((size_t)b * Hq + h0 + hh) * NS + s0) * (D + 2);
+    float* dst = part + (((size_t)b * Hq + h0 + hh) * NS + s0) * (D + kPartHead);
     for (int x = lane; x < D; x += 64) {
       const int p8 = x / 8, e = x % 8;
       float acc = 0.f;
       for (int r2 = 0; r2 < RPV; ++r2) acc += ored[r2 * PARTS + p8][e];
-      dst[2 + x] = acc;
+      dst[kPartHead + x] = acc;
     }
     if (lane == 0) { dst[0] = m[hh]; dst[1] = l[hh]; }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -678,19 +683,27 @@ __global__ __launch_bounds__(64) void decode_attend_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------- combine
-// Per (sequence, q head): the slices' (m_s, l_s), one slice per lane, their weights exp2(m_s - M) by
-// wave reductions, then out = sum_s w_s o_s / sum_s w_s l_s with the columns of 64 / XPL slices in
-// flight at once.
+// Per (sequence, q head), one workgroup of 256 threads: the slices' (m_s, l_s), one slice per thread,
+// their weights exp2(m_s - M) by block reductions; then out = sum_s w_s o_s / sum_s w_s l_s, each thread
+// summing one 4-column group of o over every (256 / (D / 4))-th slice with 16-byte loads, the groups'
+// row sums added through LDS.
+constexpr int kCombineThreads = 256;
 template <typename T, int D, bool GROUPED>
-__global__ __launch_bounds__(64) void decode_combine_kernel(
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ ntok, int Hq, int Hkv, int NS, int NSg,
     T* __restrict__ out,
     const T* __restrict__ q, const T* __restrict__ k, const int4* __restrict__ pend, int Cmax,
     int32_t* __restrict__ seq_len, int32_t* __restrict__ num_closed, int32_t* __restrict__ chunk_start,
     float* __restrict__ q_run, float* __restrict__ k_run, int32_t* __restrict__ status) {
-  constexpr int XPL = (D + 63) / 64;              // output columns per lane
+  constexpr int NT = kCombineThreads, NWV = NT / 64;
+  constexpr int C4 = D / 4;                       // 4-column groups of a row
+  constexpr int SPR = NT / C4;                    // slices summed side by side
+  constexpr int RS = D + kPartHead;               // floats per partial state
+  static_assert(kDecodeGridSlices <= NT, "one slice per thread for the weights");
   __shared__ float wgt[kDecodeGridSlices];
-  const int bh = blockIdx.x, lane = threadIdx.x;
+  __shared__ float red[2][NWV];
+  __shared__ float4 acc4[SPR][C4];
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int b = bh / Hq, h = bh % Hq;
   const int G = Hq / Hkv;
   const size_t row = (size_t)b * (GROUPED ? Hkv : Hq) + (GROUPED ? h / G : h);
@@ -704,77 +717,79 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
     const bool cut = pd.y != 0;
     float* qr = q_run + (size_t)bh * D;
     const T* qn = q + (size_t)bh * D;
-    for (int x = lane; x < D; x += 64) qr[x] = cut ? to_f(qn[x]) : qr[x] + to_f(qn[x]);
+    for (int x = tid; x < D; x += NT) qr[x] = cut ? to_f(qn[x]) : qr[x] + to_f(qn[x]);
     if (h % G == 0) {
       float* kr = k_run + ((size_t)b * Hkv + h / G) * D;
       const T* kn = k + ((size_t)b * Hkv + h / G) * D;
-      for (int x = lane; x < D; x += 64) kr[x] = cut ? to_f(kn[x]) : kr[x] + to_f(kn[x]);
+      for (int x = tid; x < D; x += NT) kr[x] = cut ? to_f(kn[x]) : kr[x] + to_f(kn[x]);
     }
-    if (h == 0 && lane == 0) {
+    if (h == 0 && tid == 0) {
       seq_len[b] = pd.z + 1;
       if (cut) {
         num_closed[b] = pd.w + 1;
         chunk_start[(size_t)b * (Cmax + 1) + pd.w + 1] = pd.z;
       }
     }
-  } else if (pd.x > 0 && h == 0 && lane == 0) {
+  } else if (pd.x > 0 && h == 0 && tid == 0) {
     status[b] = pd.x;
   }
   if (n == 0) {                                   // stopped sequence (no kept token): zeros
-    for (int x = lane; x < D; x += 64) from_f(0.f, op[x]);
+    for (int x = tid; x < D; x += NT) from_f(0.f, op[x]);
     return;
   }
   // partial states: one per attention wave that had a slice (wave s0 took slices s0, s0 + NSg, ...)
-  const int nsl = min((n + kDecodeSlice - 1) / kDecodeSlice, NSg);   // <= NS
-  const float* pp = part + (size_t)bh * NS * (D + 2);
-  // slice lane in registers; slices past 64 (rows over 64 slices) are read again for their weights
-  const float m0 = lane < nsl ? pp[(size_t)lane * (D + 2)] : -INFINITY;
-  const float l0 = lane < nsl ? pp[(size_t)lane * (D + 2) + 1] : 0.f;
-  float M = m0;
-  for (int sl = 64 + lane; sl < nsl; sl += 64) M = fmaxf(M, pp[(size_t)sl * (D + 2)]);
-  M = wave_max(M);
-  float Lpart = 0.f;
-  if (lane < nsl) {
-    const float w = exp2f(m0 - M);
-    wgt[lane] = w;
-    Lpart = w * l0;
-  }
-  for (int sl = 64 + lane; sl < nsl; sl += 64) {
-    const float w = exp2f(pp[(size_t)sl * (D + 2)] - M);
-    wgt[sl] = w;
-    Lpart += w * pp[(size_t)sl * (D + 2) + 1];
-  }
-  const float inv = 1.0f / wave_add(Lpart);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  float acc[XPL];
+  const int nsl = min((n + kDecodeSlice - 1) / kDecodeSlice, NSg);   // <= NS <= kDecodeGridSlices
+  const float* pp = part + (size_t)bh * NS * RS;
+  const float m0 = tid < nsl ? pp[(size_t)tid * RS] : -INFINITY;
+  const float l0 = tid < nsl ? pp[(size_t)tid * RS + 1] : 0.f;
+  float M = wave_max(m0);
+  if (lane == 0) red[0][wv] = M;
+  __syncthreads();
 #pragma unroll
-  for (int i = 0; i < XPL; ++i) acc[i] = 0.f;
-  for (int s0 = 0; s0 < nsl; s0 += 64) {
-    const int cnt = min(64, nsl - s0);
-    float v[XPL][64 / XPL];
-    // columns x = lane + 64 i of slices s0 .. s0 + cnt - 1, all loads of a batch issued before use
-    for (int s1 = 0; s1 < cnt; s1 += 64 / XPL) {
+  for (int x = 0; x < NWV; ++x) M = fmaxf(M, red[0][x]);
+  const float w = tid < nsl ? exp2f(m0 - M) : 0.f;
+  if (tid < nsl) wgt[tid] = w;
+  float Ls = wave_add(w * l0);
+  if (lane == 0) red[1][wv] = Ls;
+  __syncthreads();
+  Ls = 0.f;
 #pragma unroll
-      for (int j = 0; j < 64 / XPL; ++j)
+  for (int x = 0; x < NWV; ++x) Ls += red[1][x];     // same order in every thread
+  const float inv = 1.0f / Ls;
+  // o: thread (r, c) sums columns 4c .. 4c + 3 of slices r, r + SPR, ..., four loads in flight
+  const int c = tid % C4, r = tid / C4;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = r; s0 < nsl; s0 += 4 * SPR) {
+    float4 v[4];
+    float ww[4];
 #pragma unroll
-        for (int i = 0; i < XPL; ++i) {
-          const int x = lane + 64 * i;
-          const int sl = s0 + s1 + j;
-          v[i][j] = (x < D && s1 + j < cnt) ? pp[(size_t)sl * (D + 2) + 2 + x] : 0.f;
-        }
+    for (int j = 0; j < 4; ++j) {
+      const int sl = s0 + j * SPR;
+      v[j] = sl < nsl ? *reinterpret_cast<const float4*>(pp + (size_t)sl * RS + kPartHead + 4 * c)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+      ww[j] = sl < nsl ? wgt[sl] : 0.f;
+    }
 #pragma unroll
-      for (int j = 0; j < 64 / XPL; ++j)
-#pragma unroll
-        for (int i = 0; i < XPL; ++i)
-          if (s1 + j < cnt) acc[i] = fmaf(wgt[s0 + s1 + j], v[i][j], acc[i]);
+    for (int j = 0; j < 4; ++j) {
+      a.x = fmaf(ww[j], v[j].x, a.x);
+      a.y = fmaf(ww[j], v[j].y, a.y);
+      a.z = fmaf(ww[j], v[j].z, a.z);
+      a.w = fmaf(ww[j], v[j].w, a.w);
     }
   }
+  acc4[r][c] = a;
+  __syncthreads();
+  if (tid < C4) {
+    float4 t = acc4[0][tid];
 #pragma unroll
-  for (int i = 0; i < XPL; ++i) {
-    const int x = lane + 64 * i;
-    if (x < D) from_f(acc[i] * inv, op[x]);
+    for (int x = 1; x < SPR; ++x) {
+      const float4 u = acc4[x][tid];
+      t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+    }
+    from_f(t.x * inv, op[4 * tid]);
+    from_f(t.y * inv, op[4 * tid + 1]);
+    from_f(t.z * inv, op[4 * tid + 2]);
+    from_f(t.w * inv, op[4 * tid + 3]);
   }
 }
 
@@ -881,7 +896,8 @@ hipError_t step_d(const DecodeDims& p, const DecodePtrs& s, const void* q, const
   }
 #undef DHSA_ATTEND
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL((decode_combine_kernel<T, D, GROUPED>), dim3(p.B * p.Hq), dim3(64), 0, stream, w.part, w.ntok,
+  hipLaunchKernelGGL((decode_combine_kernel<T, D, GROUPED>), dim3(p.B * p.Hq), dim3(kCombineThreads), 0, stream,
+                     w.part, w.ntok,
                      p.Hq, p.Hkv, w.NS, NSg, (T*)out, (const T*)q, (const T*)k, (const int4*)w.pend, p.Cmax,
                      s.seq_len,
                      s.num_closed, s.chunk_start, s.q_run, s.k_run, s.status);
