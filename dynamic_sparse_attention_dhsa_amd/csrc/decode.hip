@@ -221,9 +221,49 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(
   int code = status[b] != 0 ? -1 : (t >= L ? 1 : 0);   // -1 stopped before, 1 cache full, 2 table full
   const T* kn = k + (size_t)b * Wk;
   T* kc = k_cache + (size_t)b * L * Wk;
+  // this thread's first elements of the previous key row and of the new one, for the similarity
+  // (unconditional loads, from the new row's first element where this thread has none, so nothing
+  // consumes them before the loads below are issued)
+  const bool app = code == 0 && t > 0;
+  const bool pld = app && tid < Wk;
+  const T pa = *(pld ? kc + (size_t)(t - 1) * Wk + tid : kn);
+  const T pc = *(pld ? kn + tid : kn);
+  // Loads that do not depend on the append decision go out next, so they are in flight while it is
+  // taken: the first batch of this wave's closed-chunk key summaries (read across lanes: LS lanes x 16
+  // bytes per summary row, RS rows per load, 16 loads per batch) and this thread's query-sum inputs.
+  constexpr int LS = D / 4, RS = 64 / LS;
+  const int sr = lane / LS, sp = lane % LS;
+  const int per_wave = (nc0 + kRouteThreads / 64 - 1) / (kRouteThreads / 64);
+  const int j_lo = wv * per_wave, j_hi = min(nc0, j_lo + per_wave);
+  float4 kv[16];
+  auto load_sums = [&](int j0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      const int j = j0 + x * RS + sr;
+      kv[x] = j < j_hi ? *reinterpret_cast<const float4*>(k_sum + (((size_t)b * Cmax + j) * Hkv + g) * D + 4 * sp)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  load_sums(j_lo);
+  constexpr int QH = GROUPED ? 8 : 1;             // query heads summed into the row's summary, at most
+  float qrv[QH];
+  T qnv[QH];                                      // (unconditional loads, converted where used)
+  const float* qr = q_run + (size_t)b * Wq;
+  const T* qn = q + (size_t)b * Wq;
+#pragma unroll
+  for (int hh = 0; hh < QH; ++hh) {
+    const bool in = tid < D && (GROUPED ? hh < G : hh == 0);
+    const int y = in ? ((GROUPED ? g * G : r) + hh) * D + tid : 0;
+    qrv[hh] = qr[y];
+    qnv[hh] = qn[y];
+  }
   float dot = 0.f, na = 0.f, nb = 0.f;
-  if (code == 0 && t > 0) {
-    for (int x = tid; x < Wk; x += kRouteThreads) {
+  if (app) {
+    const float fa = pld ? to_f(pa) : 0.f, fc = pld ? to_f(pc) : 0.f;
+    dot = fmaf(fa, fc, dot);
+    na = fmaf(fa, fa, na);
+    nb = fmaf(fc, fc, nb);
+    for (int x = tid + kRouteThreads; x < Wk; x += kRouteThreads) {
       const float a = to_f(kc[(size_t)(t - 1) * Wk + x]), c = to_f(kn[x]);
       dot = fmaf(a, c, dot);
       na = fmaf(a, a, na);
@@ -272,41 +312,27 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(
   if (r == 0 && tid == 0) pend[b] = make_int4(0, cut ? 1 : 0, t, nc0);
   // the open chunk's query summary with this token
   const float inv = 1.0f / sqrtf((float)(t_end - c0));
-  const float* qr = q_run + (size_t)b * Wq;
-  const T* qn = q + (size_t)b * Wq;
-  for (int x = tid; x < D; x += kRouteThreads) {
-    float a;
-    if constexpr (GROUPED) {
-      a = 0.f;
-      for (int hh = 0; hh < G; ++hh) {
-        const int y = (g * G + hh) * D + x;
+  if (tid < D) {
+    float a = 0.f;
+#pragma unroll
+    for (int hh = 0; hh < QH; ++hh)
+      if (GROUPED ? hh < G : hh == 0) a += (cut ? to_f(qnv[hh]) : qrv[hh] + to_f(qnv[hh])) * inv;
+    if constexpr (GROUPED) {                      // groups of more than QH heads: the rest loaded here
+      for (int hh = QH; hh < G; ++hh) {
+        const int y = (g * G + hh) * D + tid;
         a += (cut ? to_f(qn[y]) : qr[y] + to_f(qn[y])) * inv;
       }
-    } else {
-      const int y = r * D + x;
-      a = (cut ? to_f(qn[y]) : qr[y] + to_f(qn[y])) * inv;
     }
-    qv[x] = a;
+    qv[tid] = a;
   }
   __syncthreads();
   const int kk = min(topk, nc);
   if (kk < nc && kk > 0) {
-    // key summaries read across lanes: LS lanes x 16 bytes per summary row, RS rows per load, 16
-    // loads in flight per wave; each lane's partial dot product summed over its row's lanes
-    constexpr int LS = D / 4, RS = 64 / LS;
-    const int sr = lane / LS, sp = lane % LS;
+    // chunks closed before this token: summaries in memory, the first batch already loaded; each
+    // lane's partial dot product summed over its row's lanes
     const float4 q4 = *reinterpret_cast<const float4*>(&qv[4 * sp]);
-    // chunks closed before this token: summaries in memory
-    const int per_wave = (nc0 + kRouteThreads / 64 - 1) / (kRouteThreads / 64);
-    const int j_lo = wv * per_wave, j_hi = min(nc0, j_lo + per_wave);
     for (int j0 = j_lo; j0 < j_hi; j0 += 16 * RS) {
-      float4 kv[16];
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const int j = j0 + x * RS + sr;
-        kv[x] = j < j_hi ? *reinterpret_cast<const float4*>(k_sum + (((size_t)b * Cmax + j) * Hkv + g) * D + 4 * sp)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+      if (j0 != j_lo) load_sums(j0);
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
         float a = q4.x * kv[x].x;

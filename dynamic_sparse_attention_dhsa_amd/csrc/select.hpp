@@ -21,6 +21,17 @@ __device__ inline uint32_t ordered_bits(float s) {
 }
 
 
+// Sum of x over the wave on the DPP paths (the total lands in lane 63, read back for every lane).
+__device__ inline int wave_sum_i32(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  x += __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  x += __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false);  // row_mirror
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
 // Selection over the scores held in registers (ob[b]: ordered bits of candidate first + 64 b +
 // lane, 0 where there is no candidate; a finite score never maps to 0 and every trial value is at
 // least 1, so empty slots never count).  NB is the number of batches in use, fixed at compile time
@@ -28,14 +39,36 @@ __device__ inline uint32_t ordered_bits(float s) {
 template <int NB>
 __device__ inline void select_and_write(const uint32_t (&ob)[kSelBatches], int kk, int first, int lane,
                                         int32_t* __restrict__ out) {
-  // thr: the largest value with at least kk candidates at or above it, i.e. the kk-th best score
+  // thr: the largest value with at least kk candidates at or above it, i.e. the kk-th best score.
+  // Few batches: one bit per step, counted with a ballot and popcount per batch.  From four batches on
+  // the steps' dependency chain (count, wave sum, threshold) is what costs, so a step settles two bits:
+  // the counts at thr | 01, thr | 10 and thr | 11 (per-lane vector counts, three wave sums in flight)
+  // are monotone, and the largest trial value that keeps kk candidates is the one the bit-by-bit
+  // search would reach.
   uint32_t thr = 0u;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t t = thr | (1u << bit);
-    int cnt = 0;
+  if constexpr (NB >= 4) {
+    for (int bit = 30; bit >= 0; bit -= 2) {
+      const uint32_t t1 = thr | (1u << bit), t2 = thr | (2u << bit), t3 = thr | (3u << bit);
+      int c1 = 0, c2 = 0, c3 = 0;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) cnt += __popcll(__ballot(ob[b] >= t));
-    if (cnt >= kk) thr = t;
+      for (int b = 0; b < NB; ++b) {
+        c1 += ob[b] >= t1 ? 1 : 0;
+        c2 += ob[b] >= t2 ? 1 : 0;
+        c3 += ob[b] >= t3 ? 1 : 0;
+      }
+      c1 = wave_sum_i32(c1);
+      c2 = wave_sum_i32(c2);
+      c3 = wave_sum_i32(c3);
+      thr = c3 >= kk ? t3 : (c2 >= kk ? t2 : (c1 >= kk ? t1 : thr));
+    }
+  } else {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t t = thr | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) cnt += __popcll(__ballot(ob[b] >= t));
+      if (cnt >= kk) thr = t;
+    }
   }
   // Write in chunk order those above thr, then the first ones equal to it until kk are written.
   int above = 0;
@@ -73,16 +106,6 @@ __device__ inline void select_dispatch(int nb, const uint32_t (&ob)[kSelBatches]
 // the kept set is {K >= X} for X the smallest value whose at-or-above length sum fits; X is found
 // bit by bit from the top: bit b stays 0 when the largest value with that bit 0 (lower bits all 1)
 // still fits.  Writes the kept indices ascending (first + 64 b + lane) and returns how many.
-__device__ inline int wave_sum_i32(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
-  x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
-  x += __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);  // row_half_mirror
-  x += __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false);  // row_mirror
-  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
-  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
-  return __builtin_amdgcn_readlane(x, 63);
-}
-
 template <int NB>
 __device__ inline int select_tokens_and_write(const uint32_t (&ob)[kSelBatches], const int (&len)[kSelBatches],
                                               int budget, int first, int lane, int32_t* __restrict__ out) {

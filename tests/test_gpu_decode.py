@@ -130,6 +130,8 @@ CASES = {
     # group sizes outside {1, 2, 4, 8} (one q head per attention wave when routing per KV head) and 8
     "bf16_d128_g3": ([SeqSpec(600, ("uniform", 24, 100), 0, 0)], 6, 2, 128, "bf16", 60, 480, 16, 120, 0.5, 3),
     "bf16_d128_g8": ([SeqSpec(600, ("uniform", 24, 100), 0, 0)], 16, 2, 128, "bf16", 61, 480, 16, 120, 0.5, 3),
+    # more than eight query heads per KV head (the routing kernel sums the heads past eight separately)
+    "bf16_d64_g16": ([SeqSpec(500, ("uniform", 24, 100), 0, 0)], 32, 2, 64, "bf16", 62, 400, 16, 120, 0.5, 3),
 }
 
 
