@@ -34,7 +34,7 @@ if ROOT not in sys.path:
 
 METRIC = "sparse-prefill tokens/s per attn layer at 128K (8B shape); % MFMA/HBM peak"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector ALU: 256 CUs x 4 SIMDs x 16 lanes x 2 (packed) x 2 FLOP x 2.4 GHz
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PREFILL_SRC = os.path.join(ROOT, "dynamic_sparse_attention_dhsa_amd", "csrc", "prefill_bf16.hip")
 
@@ -465,7 +465,7 @@ def main() -> int:
                    "num_kv_heads": Hkv, "head_dim": d, "chunks": C,
                    "topk": int(w.topk.max()) if C else 0, "routing": "per_kv_head" if grouped else "per_q_head",
                    "parallelism": "single-gpu"},
-        "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel" if bf16 else "prefill_f32_kernel",
+        "roofline": {"bound": "mfma" if bf16 else "alu", "kernel": "prefill_bf16_kernel" if bf16 else "prefill_f32_kernel",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
                      # the committed counter record is of the per-q-head lists (bench_traffic.py)
                      "traffic": traffic_record(w.name) if bf16 and not grouped else None,
