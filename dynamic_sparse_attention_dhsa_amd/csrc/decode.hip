@@ -357,10 +357,72 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(
   __syncthreads();
   // more closed chunks than a wave holds in registers: the workgroup selects (kk, nc block-uniform)
   if (kk > 0 && kk < nc && nc > sel::kSelCand) block_select(scores, nc, kk, kl, sel_cnt, tid);
+  // Between NBW and kSelCand / 64 batches of 64 candidates, the candidates are first narrowed by several
+  // waves at once: wave w finds the kk-th best key among its own NBW batches (chunks 64 NBW w ..), and
+  // since the row's kk-th best is at least the largest of these local values L, only keys >= L can be
+  // kept.  Those are compacted into LDS in chunk order (so ties keep their order), and wave 0 selects
+  // among them exactly as among all: the same kept set.
+  constexpr int NBW = 4;
+  const bool narrow = kk > 0 && kk < nc && nc > 64 * NBW && nc <= sel::kSelCand;
+  uint32_t* cbits = reinterpret_cast<uint32_t*>(scores);           // (the scores are no longer read
+  int32_t* cidx = reinterpret_cast<int32_t*>(scores + sel::kSelCand);  // once narrowing has begun)
+  int ncand = 0;
+  if (narrow) {                                   // block-uniform
+    uint32_t x[NBW];
+    int nw = 0;
+#pragma unroll
+    for (int bt = 0; bt < NBW; ++bt) {
+      const int j = 64 * (NBW * wv + bt) + lane;
+      x[bt] = j < nc ? sel::ordered_bits(scores[j]) : 0u;
+      nw += __popcll(__ballot(x[bt] != 0u));
+    }
+    uint32_t lw = 0u;                             // this wave's kk-th best key (0: fewer than kk here)
+    if (nw > kk) {
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t t = lw | (1u << bit);
+        int c = 0;
+#pragma unroll
+        for (int bt = 0; bt < NBW; ++bt) c += __popcll(__ballot(x[bt] >= t));
+        if (c >= kk) lw = t;
+      }
+    }
+    if (lane == 0) sel_cnt[0][wv] = (int)lw;
+    __syncthreads();
+    uint32_t Lb = 0u;
+#pragma unroll
+    for (int w = 0; w < kRouteWaves; ++w) Lb = max(Lb, (uint32_t)sel_cnt[0][w]);
+    uint64_t km[NBW];
+    int cw = 0;
+#pragma unroll
+    for (int bt = 0; bt < NBW; ++bt) {
+      km[bt] = __ballot(x[bt] != 0u && x[bt] >= Lb);
+      cw += __popcll(km[bt]);
+    }
+    if (lane == 0) sel_cnt[1][wv] = cw;
+    __syncthreads();                              // every wave has read slot 0 and the scores
+    int base = 0;
+#pragma unroll
+    for (int w = 0; w < kRouteWaves; ++w) {
+      const int c = sel_cnt[1][w];
+      base += w < wv ? c : 0;
+      ncand += c;
+    }
+    const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int bt = 0; bt < NBW; ++bt) {
+      if ((km[bt] >> lane) & 1ull) {
+        const int pos = base + __popcll(km[bt] & below);
+        cbits[pos] = x[bt];
+        cidx[pos] = 64 * (NBW * wv + bt) + lane;
+      }
+      base += __popcll(km[bt]);
+    }
+    __syncthreads();
+  }
   if (tid < 64) {                                 // wave 0 selects (or finds kl written) and lays out spans
     if (kk == nc) {
       for (int x = lane; x < nc; x += 64) kl[x] = x;
-    } else if (kk > 0 && nc <= sel::kSelCand) {
+    } else if (kk > 0 && nc <= 64 * NBW) {          // few candidates: wave 0 selects among all directly
       uint32_t ob[sel::kSelBatches];
       const int nb = (nc + 63) >> 6;
 #pragma unroll
@@ -369,6 +431,19 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(
         ob[bt] = (bt < nb && j < nc) ? sel::ordered_bits(scores[j]) : 0u;
       }
       sel::select_dispatch<1>(nb, ob, kk, 0, lane, kl);
+    } else if (narrow) {
+      uint32_t ob[sel::kSelBatches];
+      const int nb = (ncand + 63) >> 6;
+#pragma unroll
+      for (int bt = 0; bt < sel::kSelBatches; ++bt) {
+        const int p = 64 * bt + lane;
+        ob[bt] = (bt < nb && p < ncand) ? cbits[p] : 0u;
+      }
+      sel::select_dispatch<1>(nb, ob, kk, 0, lane, kl);   // positions in the candidate list
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      for (int x = lane; x < kk; x += 64) kl[x] = cidx[kl[x]];
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();

@@ -218,6 +218,16 @@ def test_decode_32k_context():
     _check(seqs, 32, 8, 128, "bf16", 60, 32768, 32, 1024, 0.5, 32, grouped=False)
 
 
+@pytest.mark.parametrize("grouped", [False, True])
+def test_decode_narrowed_selection(grouped):
+    """A 16K-token context in chunks of 24..40 tokens: about 500 closed chunks, between the direct and
+    the workgroup-wide selections, so routing first narrows the candidates across waves (each wave's
+    own top-k bound) and then selects among the survivors.  Outputs, kept lists and the final chunk
+    table against the decode oracle."""
+    seqs = [SeqSpec(16384 + 12, ("uniform", 24, 40), 0, 0)]
+    _check(seqs, 4, 2, 64, "bf16", 64, 16384, 16, 64, 0.5, 32, grouped=grouped, C=1024)
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("grouped", [False, True])
 def test_decode_128k_context_beyond_1024_chunks(grouped):
