@@ -553,6 +553,11 @@ __global__ __launch_bounds__(64) void decode_attend_kernel(
   const T* kb = k_cache + ((size_t)b * L * Hkv + g) * D;      // row u at kb + u * Hkv * D
   const T* vb = v_cache + ((size_t)b * L * Hkv + g) * D;
   const size_t rs = (size_t)Hkv * D;
+  const uint32_t rsb = (uint32_t)(rs * sizeof(T));            // bytes between consecutive tokens' rows
+  // a cache row's key (value) address: one 32 x 32 -> 64-bit multiply-add
+  auto row_ptr = [rsb](const T* base, int u) __attribute__((always_inline)) {
+    return reinterpret_cast<const uint8_t*>(base) + (uint64_t)(uint32_t)u * rsb;
+  };
   const int32_t* ur = urow + row * (size_t)L;
   const int kr = lane / LPR, kp = lane % LPR;     // key row within an instruction, piece of the row
   const int vg = lane / PARTS, vp = lane % PARTS; // value row within an instruction, part of the row
@@ -601,12 +606,17 @@ __global__ __launch_bounds__(64) void decode_attend_kernel(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     const int nblk = (hi_tok - lo_tok + 63) / 64;
     uint4 kraw[KB];
+    // Loads are unconditional (a load under a per-lane condition costs an exec-mask branch): a row
+    // past the slice's end loads the block's first row instead, a kept token, so finite wherever the
+    // result is; its score is replaced by -inf and its weight is 0.
     auto issue_k = [&](int bk, int j0) __attribute__((always_inline)) {
+      const int r0 = rowbuf[bk][0];
+      int uu[KB];
 #pragma unroll
-      for (int jj = 0; jj < KB; ++jj) {
-        const int u = rowbuf[bk][(j0 + jj) * RPI + kr];
-        kraw[jj] = u >= 0 ? *reinterpret_cast<const uint4*>(kb + (size_t)u * rs + kp * EPL) : make_uint4(0, 0, 0, 0);
-      }
+      for (int jj = 0; jj < KB; ++jj) uu[jj] = rowbuf[bk][(j0 + jj) * RPI + kr];
+#pragma unroll
+      for (int jj = 0; jj < KB; ++jj)
+        kraw[jj] = *reinterpret_cast<const uint4*>(row_ptr(kb, uu[jj] >= 0 ? uu[jj] : r0) + kp * 16);
     };
     auto score_k = [&](int j0) __attribute__((always_inline)) {
 #pragma unroll
@@ -652,13 +662,16 @@ __global__ __launch_bounds__(64) void decode_attend_kernel(
     // value loads: rows j * RPV + vg, VJB row steps in flight (one or two 16-byte loads each)
     uint4 vraw[VJB][VW];
     auto issue_v = [&](int bk, int j0) __attribute__((always_inline)) {
+      const int r0 = rowbuf[bk][0];
+      int vv[VJB];
+#pragma unroll
+      for (int jj = 0; jj < VJB; ++jj) vv[jj] = rowbuf[bk][(j0 + jj) * RPV + vg];
 #pragma unroll
       for (int jj = 0; jj < VJB; ++jj) {
-        const int vr = rowbuf[bk][(j0 + jj) * RPV + vg];
+        const int vr = vv[jj] >= 0 ? vv[jj] : r0;
 #pragma unroll
         for (int x = 0; x < VW; ++x)
-          vraw[jj][x] = vr >= 0 ? *reinterpret_cast<const uint4*>(vb + (size_t)vr * rs + vp * 8 + x * EPL)
-                                : make_uint4(0, 0, 0, 0);
+          vraw[jj][x] = *reinterpret_cast<const uint4*>(row_ptr(vb, vr) + vp * 8 * sizeof(T) + x * 16);
       }
     };
     auto accum_v = [&](int j0) __attribute__((always_inline)) {
@@ -692,7 +705,7 @@ __global__ __launch_bounds__(64) void decode_attend_kernel(
                                __uint_as_float(vraw[jj][1].z), __uint_as_float(vraw[jj][1].w)};
 #pragma unroll
           for (int hh = 0; hh < GH; ++hh) {
-            const float pw = pbuf[hh][tt];       // 0 for rows past the slice (zero values too)
+            const float pw = pbuf[hh][tt];       // 0 for rows past the slice
 #pragma unroll
             for (int e = 0; e < 8; ++e) o[hh][e] = fmaf(pw, vf[e], o[hh][e]);
           }
