@@ -1,7 +1,7 @@
 // Stage 3: block-sparse causal prefill, bf16 in, fp32 accumulate, on gfx950 MFMA.
 //
-// ICML 2026 spotlight page (Abstract): DHSA runs attention through a
-// memory-efficient tiled backend over the interactions its router keeps;
+// ICML 2026 spotlight page (Abstract): DHSA computes attention over the
+// interactions its router keeps with a tiled kernel that keeps memory low;
 // "... for On-Device LLMs" (Abstract): the kept token interactions follow from
 // chunk scores upsampled to token level.  Query token t of chunk i, head h
 // attends to every key u <= t inside a kept chunk of row (h, i):

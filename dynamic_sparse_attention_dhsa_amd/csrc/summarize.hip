@@ -2,7 +2,7 @@
 //
 // "Long-Context Modeling with Dynamic Hierarchical Sparse Attention for
 // On-Device LLMs" (Abstract, Innovation): a chunk is represented by the
-// average of its token vectors scaled by the square root of its size, i.e.
+// mean of its token vectors times sqrt(n) for a chunk of n tokens, i.e.
 //   sum[c, h, :] = (sum over tokens t of chunk c of x[t, h, :]) / sqrt(n_c).
 //
 // In the packed THD layout the tokens of chunk c form one contiguous block of

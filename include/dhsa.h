@@ -3,7 +3,7 @@
  *
  * Dynamic Hierarchical Sparse Attention splits each sequence into
  * variable-length chunks, represents every chunk by the average of its token
- * vectors scaled by the square root of the chunk size, scores chunk pairs
+ * vectors times sqrt(n) for a chunk of n tokens, scores chunk pairs
  * causally, upsamples the chunk scores to token level and runs exact softmax
  * attention over the token interactions that survive ("Long-Context Modeling
  * with Dynamic Hierarchical Sparse Attention for On-Device LLMs", Abstract and

@@ -12,7 +12,7 @@ What it follows (the pages are two versions of one paper):
        Memory-Constrained LLM Inference" (ICML 2026 spotlight page): Abstract.
 The steps, in the pages' order: the sequence is split into variable-length
 chunks; each chunk gets a representation by aggregating its token vectors,
-the average scaled by the square root of the chunk size [P2 Abstract,
+the mean times sqrt(n) for a chunk of n tokens [P2 Abstract,
 Innovation]; chunk-level similarity is computed [P2 Abstract] causally
 [P3 Abstract]; the chunk scores are upsampled to token level and the
 resulting importance decides which token interactions are kept [P2 Abstract,
