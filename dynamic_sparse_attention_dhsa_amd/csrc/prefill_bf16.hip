@@ -327,6 +327,15 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
       if (coff >= clen) cj = -1;
       return t;
     }
+    // the common case: the whole tile inside the current chunk (one key range, no partial group)
+    if (clen - coff >= BK) {
+      t.nval = ckeep ? kFull : 0ull;
+#pragma unroll
+      for (int m = 0; m < GE::DPW; ++m) t.src[m] = cr0 + coff + GS * (wave * GE::DPW + m);
+      coff += BK;
+      if (coff >= clen) enter(rf(next_set(bm[kUnion], cj + 1, nbits)));
+      return t;
+    }
     int slot = 0;
     while (slot < NGRP) {                    // pack groups from consecutive kept chunks
       const int left = clen - coff;
