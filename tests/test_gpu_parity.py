@@ -178,6 +178,18 @@ SMALL = {
                                   6, 2, 128, "bf16", 19, "g3"),
     "bf16_d128_g16": lambda: small([SeqSpec(900, ("uniform", 24, 200), 5, 2)], 32, 2, 128, "bf16", 20, "g16",
                                    topics_per_head=True),
+    # chunk lengths on both sides of the key tile (64 keys at d = 64 and 128, 32 at d = 256) and of the
+    # staging group (8, 4 and 2 rows): tiles that lie inside one chunk, tiles that pack the ends of
+    # several, short groups at chunk ends, chunks that some heads of a group keep and others do not
+    "bf16_d128_tile_edges": lambda: small(
+        [SeqSpec(1303, ("explicit", [63, 64, 65, 1, 127, 128, 129, 3, 4, 5, 66, 130, 62, 200, 64, 64, 31, 97]), 7, 2)],
+        8, 2, 128, "bf16", 22, "tile_edges_d128", topics_per_head=True),
+    "bf16_d256_tile_edges": lambda: small(
+        [SeqSpec(838, ("explicit", [31, 32, 33, 1, 63, 64, 65, 2, 3, 95, 96, 97, 34, 30, 160, 32]), 6, 2)],
+        4, 2, 256, "bf16", 23, "tile_edges_d256", topics_per_head=True),
+    "bf16_d64_tile_edges": lambda: small(
+        [SeqSpec(713, ("explicit", [7, 8, 9, 63, 64, 65, 1, 15, 16, 17, 127, 128, 129, 64]), 5, 2)],
+        8, 2, 64, "bf16", 24, "tile_edges_d64", topics_per_head=True),
 }
 
 
@@ -209,7 +221,7 @@ def test_small_end_to_end(small_case):
 # routing once per KV head: the group's row, checked against the oracle's grouped routing, and the
 # whole path end to end with it
 GROUPED = ("bf16_d128_g4_ragged", "bf16_d128_g8_long_chunks", "bf16_d256_g2", "bf16_d64_g1", "bf16_divergent_heads",
-           "f32_d128_g2", "bf16_d128_g3", "bf16_d128_g16")
+           "f32_d128_g2", "bf16_d128_g3", "bf16_d128_g16", "bf16_d128_tile_edges", "bf16_d256_tile_edges")
 
 
 @pytest.mark.parametrize("name", GROUPED)
