@@ -9,12 +9,14 @@
 //   a chunk starting at c0 in a sequence ending at e ends at the first t in
 //   [c0 + lo, min(c0 + hi, e)) with sim[t] < tau, else at min(c0 + hi, e).
 //
-// Kernel 1 (HBM-bound): a wave covers 64 consecutive tokens, with its lanes
-// spread across the key row (16-byte loads, so each load instruction reads one
-// contiguous span of the row); the previous row stays in registers, so every
-// row is read once.  Per token the dot product and the two squared norms are
-// reduced across the wave in fp32; the lane of the token writes sim and the
-// cut decisions go into the word's bits by a ballot.
+// Kernel 1 (HBM-bound): a wave covers 8 consecutive tokens, all their rows in
+// flight at once (at rows of up to 2 KB), with its lanes spread across the key
+// row (16-byte loads, so each load instruction reads one contiguous span of the
+// row); the previous row stays in registers, so a row is read once per wave.
+// Per token the dot product with the previous row and the row's squared norm
+// (packed bf16 dot products for bf16 rows) are reduced across the wave in fp32,
+// the previous row's norm being the last token's; the lane of the token writes
+// sim, and the wave's cut decisions are one byte of a bitmap word.
 // Kernel 2 (latency-bound, one workgroup): the greedy walk, split into segments
 // walked speculatively by 16 waves and stitched by one (walks from different
 // starts merge at their first common cut); a window of 64 bitmap words (4096
@@ -25,8 +27,10 @@
 namespace dhsa {
 namespace {
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kSimWaves = 4;
-constexpr int kSimTok = 16;                       // tokens per wave of the similarity kernel
+constexpr int kSimTok = 8;                        // tokens per wave of the similarity kernel: one byte of a bitmap word
 
 __device__ inline int seq_of_token(const int32_t* __restrict__ cu_seqlens, int B, int t) {
   int lo = 0, hi = B - 1;                         // last b with cu_seqlens[b] <= t
@@ -72,18 +76,18 @@ __device__ inline float wave_sum(float x) {
 
 // NJ 16-byte pieces per lane cover the row (pieces j * 64 + lane; lanes past the row's end idle).
 // A wave takes kSimTok consecutive tokens with R rows in flight: a ring of R row buffers, each refilled
-// with the row R tokens ahead as soon as it has been consumed (refills past the wave's last token
-// re-read that token, a cache hit).  Its kSimTok cut bits are one 16-bit quarter of a bitmap word.
+// with the row R tokens ahead as soon as it has been consumed.  Its kSimTok cut bits are one byte of a
+// bitmap word.
 template <typename T, int NJ, int R>
 __global__ __launch_bounds__(kSimWaves * 64) void adjacent_sim_kernel(
     const T* __restrict__ k, const int32_t* __restrict__ cu_seqlens, int B, int ntok, int W, float tau,
-    float* __restrict__ sim, uint16_t* __restrict__ cut_quarters) {
+    float* __restrict__ sim, uint8_t* __restrict__ cut_bytes) {
   constexpr int VEC = 16 / sizeof(T);             // elements per 16-byte load
   const int lane = threadIdx.x & 63;
   const int part = blockIdx.x * kSimWaves + (threadIdx.x >> 6);
   const int t0 = part * kSimTok;
-  if (t0 >= ntok) {                               // wave-uniform: a quarter past T in the last word
-    if (lane == 0 && part < (ntok + 63) / 64 * (64 / kSimTok)) cut_quarters[part] = 0;
+  if (t0 >= ntok) {                               // wave-uniform: a byte past T in the last word
+    if (lane == 0 && part < (ntok + 63) / 64 * (64 / kSimTok)) cut_bytes[part] = 0;
     return;
   }
   const int npieces = W / VEC;
@@ -101,16 +105,51 @@ __global__ __launch_bounds__(kSimWaves * 64) void adjacent_sim_kernel(
       x[j] = p < npieces ? row[p] : make_uint4(0u, 0u, 0u, 0u);
     }
   };
-  uint4 ring[R][NJ];
-  float prv[NJ][VEC];
-  {
-    uint4 raw[NJ];
-    load_row(t0 > 0 ? t0 - 1 : 0, raw);
+  constexpr bool BF = sizeof(T) == 2;
+  // bf16: packed dot products of the rows as loaded (exact products, fp32 sums); fp32: rows widened
+  // (a no-op) and multiply-added.  A lane's partial sums over its pieces: dot(prev, cur) and |cur|^2.
+  auto partials = [&](const uint4 (&pv)[NJ], const uint4 (&cu)[NJ], float& dot, float& nc)
+      __attribute__((always_inline)) {
+    dot = 0.f;
+    nc = 0.f;
+    if constexpr (BF) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) widen(raw[j], prv[j], T{});
-  }
+      for (int j = 0; j < NJ; ++j) {
+        const uint32_t a[4] = {pv[j].x, pv[j].y, pv[j].z, pv[j].w};
+        const uint32_t c[4] = {cu[j].x, cu[j].y, cu[j].z, cu[j].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16x2 av = __builtin_bit_cast(bf16x2, a[e]), cv = __builtin_bit_cast(bf16x2, c[e]);
+          dot = __builtin_amdgcn_fdot2_f32_bf16(av, cv, dot, false);
+          nc = __builtin_amdgcn_fdot2_f32_bf16(cv, cv, nc, false);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        float a[VEC], c[VEC];
+        widen(pv[j], a, T{});
+        widen(cu[j], c, T{});
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          dot = fmaf(a[e], c[e], dot);
+          nc = fmaf(c[e], c[e], nc);
+        }
+      }
+    }
+  };
+  uint4 ring[R][NJ];
+  uint4 prv[NJ];
+  load_row(t0 > 0 ? t0 - 1 : 0, prv);
 #pragma unroll
   for (int r = 0; r < R; ++r) load_row(min(t0 + r, t_end - 1), ring[r]);
+  // |row t0 - 1|^2; afterwards each token's |previous row|^2 is the last token's |row|^2
+  float na;
+  {
+    float unused;
+    partials(prv, prv, unused, na);
+    na = wave_sum(na);
+  }
   float s_mine = 1.0f;
   uint32_t bits = 0u;
   for (int t = t0; t < t_end; t += R) {
@@ -123,35 +162,23 @@ __global__ __launch_bounds__(kSimWaves * 64) void adjacent_sim_kernel(
           cur_start = next_start;
           next_start = cu_seqlens[b + 1];
         }
-        float cur[NJ][VEC];
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) widen(ring[r][j], cur[j], T{});
-        float dot = 0.f, na = 0.f, nc = 0.f;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            dot = fmaf(prv[j][e], cur[j][e], dot);
-            na = fmaf(prv[j][e], prv[j][e], na);
-            nc = fmaf(cur[j][e], cur[j][e], nc);
-          }
+        float dot, nc;
+        partials(prv, ring[r], dot, nc);
         dot = wave_sum(dot);
-        na = wave_sum(na);
         nc = wave_sum(nc);
         float s = 1.0f;
         if (tt != cur_start && na > 0.f && nc > 0.f) s = dot / (sqrtf(na) * sqrtf(nc));
         if (s < tau) bits |= 1u << (tt - t0);
         if (lane == tt - t0) s_mine = s;
+        na = nc;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) prv[j][e] = cur[j][e];
-        load_row(min(tt + R, t_end - 1), ring[r]);
+        for (int j = 0; j < NJ; ++j) prv[j] = ring[r][j];
+        if (tt + R < t_end) load_row(tt + R, ring[r]);   // (wave-uniform)
       }
     }
   }
   if (lane < t_end - t0) sim[t0 + lane] = s_mine;
-  if (lane == 0) cut_quarters[part] = (uint16_t)bits;
+  if (lane == 0) cut_bytes[part] = (uint8_t)bits;
 }
 
 // One greedy step for one wave: the chunk starting at c0, in a sequence ending at e, ends at the
@@ -288,23 +315,23 @@ __global__ __launch_bounds__(kWalkWaves * 64) void chunk_walk_kernel(
 hipError_t launch_adjacent_similarity(int B, int ntok, int W, int dtype, const int32_t* cu_seqlens, const void* k,
                                       float tau, float* sim, uint64_t* cut_bits, hipStream_t stream) {
   if (ntok == 0) return hipSuccess;
-  const int parts = (ntok + 63) / 64 * (64 / kSimTok);   // every quarter of every bitmap word
+  const int parts = (ntok + 63) / 64 * (64 / kSimTok);   // every byte of every bitmap word
   const dim3 grid((parts + kSimWaves - 1) / kSimWaves);
   const int npieces = W / (dtype == 1 ? 8 : 4);
   const int nj = (npieces + 63) / 64;             // the host allows npieces <= kSimMaxPieces
 #define DHSA_SIM_LAUNCH(TY, NJ, R)                                                                           \
   hipLaunchKernelGGL((adjacent_sim_kernel<TY, NJ, R>), grid, dim3(kSimWaves * 64), 0, stream, (const TY*)k, \
-                     cu_seqlens, B, ntok, W, tau, sim, (uint16_t*)cut_bits)
+                     cu_seqlens, B, ntok, W, tau, sim, (uint8_t*)cut_bits)
   if (dtype == 1) {
-    if (nj <= 1) DHSA_SIM_LAUNCH(uint16_t, 1, 4);
-    else if (nj <= 2) DHSA_SIM_LAUNCH(uint16_t, 2, 4);
-    else if (nj <= 4) DHSA_SIM_LAUNCH(uint16_t, 4, 2);
-    else DHSA_SIM_LAUNCH(uint16_t, 8, 1);
+    if (nj <= 1) DHSA_SIM_LAUNCH(uint16_t, 1, 8);
+    else if (nj <= 2) DHSA_SIM_LAUNCH(uint16_t, 2, 8);
+    else if (nj <= 4) DHSA_SIM_LAUNCH(uint16_t, 4, 4);
+    else DHSA_SIM_LAUNCH(uint16_t, 8, 2);
   } else {
-    if (nj <= 1) DHSA_SIM_LAUNCH(float, 1, 4);
-    else if (nj <= 2) DHSA_SIM_LAUNCH(float, 2, 4);
-    else if (nj <= 4) DHSA_SIM_LAUNCH(float, 4, 2);
-    else DHSA_SIM_LAUNCH(float, 8, 1);
+    if (nj <= 1) DHSA_SIM_LAUNCH(float, 1, 8);
+    else if (nj <= 2) DHSA_SIM_LAUNCH(float, 2, 8);
+    else if (nj <= 4) DHSA_SIM_LAUNCH(float, 4, 4);
+    else DHSA_SIM_LAUNCH(float, 8, 2);
   }
 #undef DHSA_SIM_LAUNCH
   return hipGetLastError();
