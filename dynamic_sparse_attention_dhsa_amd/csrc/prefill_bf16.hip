@@ -509,12 +509,19 @@ __global__ __launch_bounds__(Geo<D>::NT, Geo<D>::MINW) void prefill_bf16_kernel(
       // reductions as shallow trees (four independent partial results) to keep dependency chains short
       float mx;
       if constexpr (ROWS == 32) {
-        float m4[4];
+        // a tree of three-input maxima (v_max3_f32): 32 values in 16 instructions, three levels deep
+        float t[12];
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
-          m4[x] = fmaxf(fmaxf(fmaxf(sc[0][x], sc[0][x + 4]), fmaxf(sc[0][x + 8], sc[0][x + 12])),
-                        fmaxf(fmaxf(sc[1][x], sc[1][x + 4]), fmaxf(sc[1][x + 8], sc[1][x + 12])));
-        mx = col_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+        for (int x = 0; x < 10; ++x) {
+          const int a = 3 * x, b = a + 1, c = a + 2;
+          t[x] = fmaxf(fmaxf(sc[a >> 4][a & 15], sc[b >> 4][b & 15]), sc[c >> 4][c & 15]);
+        }
+        t[10] = sc[1][14];
+        t[11] = sc[1][15];
+        float u[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) u[x] = fmaxf(fmaxf(t[3 * x], t[3 * x + 1]), t[3 * x + 2]);
+        mx = col_max(fmaxf(fmaxf(fmaxf(u[0], u[1]), u[2]), u[3]));
       } else {
         mx = col_max(fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                            fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3]))));
