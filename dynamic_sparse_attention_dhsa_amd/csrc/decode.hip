@@ -22,11 +22,11 @@
 // the cache row and the closing chunk's key summary; scores of the closed
 // chunks in LDS, the radix top-k in registers up to 1024 candidates and an
 // LDS selection beyond, then the kept spans' cache rows); attend (split-K: one
-// wave per (sequence, q head, slices of kDecodeSlice kept tokens), or per
-// (sequence, KV group, slices) when routing per KV head, so the group's heads
-// read each K/V row once; key rows read across lanes with the partial dot
-// products summed on the DPP paths, online softmax in base 2 with one token per
-// lane, PV with 16-byte value loads); combine (per (sequence, q head): the
+// wave per (sequence, q head, equal range of the kept tokens), or per
+// (sequence, KV group, range) when routing per KV head, so the group's heads
+// read each K/V row once; one round of waves fills the GPU; key rows read
+// across lanes with the partial dot products summed on the DPP paths, online
+// softmax in base 2 with one token per lane, PV with 16-byte value loads); combine (per (sequence, q head): the
 // attention waves' partial softmax states, then the append's counters and
 // running sums are committed).
 #include <math.h>
@@ -501,9 +501,25 @@ __device__ inline float group_sum(float x) {
   return x;
 }
 
-// Split-K attention.  A wave owns (sequence, block of GH q heads sharing a kept row, slices s, s + S,
-// s + 2S, ... of kDecodeSlice kept tokens, S = the grid's slices per row): GH = the group when
-// routing per KV head (its heads read each K/V row once), else 1.  The kept tokens' cache rows come
+// A row of n > 0 kept tokens as 64-token blocks, dealt to the grid's nsg waves per row in equal runs:
+// attend_run blocks per wave, the fewest any split over nsg waves can give the busiest one, and
+// attend_waves waves, the fewest that take that run length (the last may take fewer blocks).
+__device__ inline int attend_run(int nsg, int n) {
+  const int nblk = (n + 63) / 64;
+  return (nblk + nsg - 1) / nsg;
+}
+__device__ inline int attend_waves(int nsg, int n) {
+  const int nblk = (n + 63) / 64, run = attend_run(nsg, n);
+  return (nblk + run - 1) / run;
+}
+
+// Split-K attention.  A wave owns (sequence, block of GH q heads sharing a kept row, one contiguous
+// range of the row's kept tokens): GH = the group when routing per KV head (its heads read each K/V
+// row once), else 1.  The row's n kept tokens, as 64-token blocks, are dealt in equal runs of
+// consecutive blocks over at most S waves (S = the grid's waves per row, which the host sizes so that
+// the whole grid is resident at once): the busiest wave has as few blocks as S waves allow, and the
+// waves end together (fixed slices dealt round robin left the last of several rounds of waves partly
+// empty).  A wave takes its range kDecodeSlice tokens at a time.  The kept tokens' cache rows come
 // from the routing kernel's row array, loaded once per slice.  Per block of 64 tokens:
 //   scores  K rows read across lanes (LPR lanes x 16 bytes per row, RPI rows per instruction, all of
 //           a block's loads in flight, the next block's issued with this block's values), each lane's
@@ -549,7 +565,9 @@ __global__ __launch_bounds__(64) void decode_attend_kernel(
   const int G = Hq / Hkv, g = h0 / G;
   const size_t row = (size_t)b * (GROUPED ? Hkv : Hq) + (GROUPED ? g : h0);
   const int n = ntok[row];
-  if (s0 * kDecodeSlice >= n) return;             // the combine reads only slices below n
+  if (s0 >= attend_waves(NSg, n)) return;         // the combine reads only those waves' states
+  const int run = 64 * attend_run(NSg, n);        // tokens per wave
+  const int r_lo = s0 * run, r_hi = min(n, r_lo + run);
   const T* kb = k_cache + ((size_t)b * L * Hkv + g) * D;      // row u at kb + u * Hkv * D
   const T* vb = v_cache + ((size_t)b * L * Hkv + g) * D;
   const size_t rs = (size_t)Hkv * D;
@@ -583,7 +601,7 @@ __global__ __launch_bounds__(64) void decode_attend_kernel(
       for (int e = 0; e < EPL; ++e) qreg[hh][e] = qs[hh][kp * EPL + e];
   }
 
-  // one running softmax state per head across all of this wave's slices (s0, s0 + NSg, ...)
+  // one running softmax state per head across all of this wave's range
   float m[GH], l[GH], o[GH][8];
 #pragma unroll
   for (int hh = 0; hh < GH; ++hh) {
@@ -592,9 +610,8 @@ __global__ __launch_bounds__(64) void decode_attend_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
   }
-  for (int s = s0; s * kDecodeSlice < n; s += NSg) {
-    const int lo_tok = s * kDecodeSlice;
-    const int hi_tok = min(n, lo_tok + kDecodeSlice);
+  for (int lo_tok = r_lo; lo_tok < r_hi; lo_tok += kDecodeSlice) {
+    const int hi_tok = min(r_hi, lo_tok + kDecodeSlice);
     // the slice's cache rows (-1 past its end), one load per block
 #pragma unroll
     for (int bk = 0; bk < NB; ++bk) {
@@ -823,6 +840,24 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
   const size_t row = (size_t)b * (GROUPED ? Hkv : Hq) + (GROUPED ? h / G : h);
   const int n = ntok[row];
   T* op = out + (size_t)bh * D;
+  // The partial states are loaded before the row's token count is known: the grid's NSg slots of the
+  // row, of which only the first attend_waves(NSg, n) were written this step.  The others hold stale
+  // (or, before a first step, arbitrary) values, which are selected away below, never used in
+  // arithmetic.  Thread (r, c) sums columns 4c .. 4c + 3 of slots r, r + SPR, ..., four in flight.
+  const float* pp = part + (size_t)bh * NS * RS;
+  const float m_raw = tid < NSg ? pp[(size_t)tid * RS] : -INFINITY;
+  const float l_raw = tid < NSg ? pp[(size_t)tid * RS + 1] : 0.f;
+  const int c = tid % C4, r = tid / C4;
+  float4 v[4];
+  auto load_o = [&](int s0, int lim) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int sl = s0 + j * SPR;
+      v[j] = sl < lim ? *reinterpret_cast<const float4*>(pp + (size_t)sl * RS + kPartHead + 4 * c)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  load_o(r, NSg);
   // commit the token's append to the state (no other kernel of the step reads these fields after the
   // routing launch): this head's query sum, the KV head's key sum (first head of its group), the
   // sequence's counters (head 0)
@@ -851,11 +886,10 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
     for (int x = tid; x < D; x += NT) from_f(0.f, op[x]);
     return;
   }
-  // partial states: one per attention wave that had a slice (wave s0 took slices s0, s0 + NSg, ...)
-  const int nsl = min((n + kDecodeSlice - 1) / kDecodeSlice, NSg);   // <= NS <= kDecodeGridSlices
-  const float* pp = part + (size_t)bh * NS * RS;
-  const float m0 = tid < nsl ? pp[(size_t)tid * RS] : -INFINITY;
-  const float l0 = tid < nsl ? pp[(size_t)tid * RS + 1] : 0.f;
+  // partial states: one per attention wave with tokens (the row's first attend_waves(NSg, n) waves)
+  const int nsl = attend_waves(NSg, n);           // <= NSg <= NS <= kDecodeGridSlices
+  const float m0 = tid < nsl ? m_raw : -INFINITY;
+  const float l0 = tid < nsl ? l_raw : 0.f;
   float M = wave_max(m0);
   if (lane == 0) red[0][wv] = M;
   __syncthreads();
@@ -870,18 +904,15 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
 #pragma unroll
   for (int x = 0; x < NWV; ++x) Ls += red[1][x];     // same order in every thread
   const float inv = 1.0f / Ls;
-  // o: thread (r, c) sums columns 4c .. 4c + 3 of slices r, r + SPR, ..., four loads in flight
-  const int c = tid % C4, r = tid / C4;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s0 = r; s0 < nsl; s0 += 4 * SPR) {
-    float4 v[4];
+    if (s0 != r) load_o(s0, nsl);
     float ww[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int sl = s0 + j * SPR;
-      v[j] = sl < nsl ? *reinterpret_cast<const float4*>(pp + (size_t)sl * RS + kPartHead + 4 * c)
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
       ww[j] = sl < nsl ? wgt[sl] : 0.f;
+      if (sl >= nsl) v[j] = make_float4(0.f, 0.f, 0.f, 0.f);   // a stale slot of the first batch
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -978,6 +1009,27 @@ __global__ __launch_bounds__(64) void decode_load_counters_kernel(
   }
 }
 
+// Single-wave workgroups of the attention kernel <T, D, GROUPED, GH> that the current GPU holds at once
+// (its compute units times the occupancy the kernel's registers and LDS allow), looked up once per GPU;
+// 0 when the runtime cannot say.
+template <typename T, int D, bool GROUPED, int GH>
+int attend_resident_waves() {
+  static std::mutex mu;
+  static int cache[kNoAllocMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoAllocMaxDevices) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_attend_kernel<T, D, GROUPED, GH>, 64, 0) !=
+        hipSuccess)
+      return 0;
+    cache[dev] = std::max(0, cus * per_cu);
+  }
+  return cache[dev];
+}
+
 template <typename T, int D, bool GROUPED>
 hipError_t step_d(const DecodeDims& p, const DecodePtrs& s, const void* q, const void* k, const void* v, int lo,
                   int hi, float tau, int topk, float scale, void* out, int32_t* kept, const DecodeWork& w,
@@ -992,14 +1044,24 @@ hipError_t step_d(const DecodeDims& p, const DecodePtrs& s, const void* q, const
   // heads per attention wave: the whole group when routing per KV head (each K/V row read once for it)
   const int G = p.Hq / p.Hkv;
   const int gh = !GROUPED ? 1 : (G == 8 ? 8 : G == 4 ? 4 : G == 2 ? 2 : 1);
-  // slices per row in the grid: enough for the kept tokens of chunks of up to hi tokens (longer rows,
-  // e.g. from a prefix chunked otherwise, loop over slices with this stride)
-  const long long need = ((long long)(topk + 1) * hi + kDecodeSlice - 1) / kDecodeSlice;
-  const int NSg = (int)std::max(1LL, std::min<long long>(w.NS, need));
+  // Waves per row: as many as the GPU holds at once over all rows (one round of waves, each with an
+  // equal share of its row), but no more than 64-token blocks in a row of kept chunks of up to hi
+  // tokens, nor than the workspace's partial states per row.  (Rows longer than that bound, e.g. from
+  // a prefix chunked otherwise, only give each wave a longer range.)
+  const long long need = ((long long)(topk + 1) * hi + 63) / 64;
+  int NSg = 1;
+  auto waves_per_row = [&](int gh_v, int resident) {
+    const long long rows = (long long)p.B * (p.Hq / gh_v);
+    const long long fit = resident > 0 ? resident / rows : need;
+    return (int)std::max(1LL, std::min<long long>({(long long)w.NS, need, fit}));
+  };
 #define DHSA_ATTEND(GHV)                                                                                         \
-  hipLaunchKernelGGL((decode_attend_kernel<T, D, GROUPED, GHV>), dim3(p.B * (p.Hq / GHV) * NSg), dim3(64), 0,   \
-                     stream, (const T*)q, (const T*)s.k_cache, (const T*)s.v_cache, w.urow, w.ntok, p.Hq, p.Hkv,  \
-                     p.L, NSg, w.NS, scale * kLog2e, w.part)
+  do {                                                                                                           \
+    NSg = waves_per_row(GHV, attend_resident_waves<T, D, GROUPED, GHV>());                                      \
+    hipLaunchKernelGGL((decode_attend_kernel<T, D, GROUPED, GHV>), dim3(p.B * (p.Hq / GHV) * NSg), dim3(64), 0, \
+                       stream, (const T*)q, (const T*)s.k_cache, (const T*)s.v_cache, w.urow, w.ntok, p.Hq,     \
+                       p.Hkv, p.L, NSg, w.NS, scale * kLog2e, w.part);                                          \
+  } while (0)
   if constexpr (GROUPED) {
     if (gh == 8) DHSA_ATTEND(8);
     else if (gh == 4) DHSA_ATTEND(4);

@@ -55,7 +55,7 @@ hipError_t launch_chunk_walk(int B, int ntok, const int32_t* cu_seqlens, const u
                              int32_t* cu_chunks, int32_t* seq_chunk_start, int32_t* num_chunks, hipStream_t stream);
 
 // Decode (one new token per sequence against the kept structure).
-constexpr int kDecodeSlice = 128;                 // kept tokens per split-K attention wave
+constexpr int kDecodeSlice = 128;                 // kept tokens a split-K attention wave stages at a time
 constexpr int kDecodeMaxChunks = DHSA_MAX_CHUNKS_PER_SEQ;   // closed chunks per sequence (scores in LDS)
 constexpr int kDecodeMaxTopk = 1024;              // topk < this: the kept list of a row
 constexpr int kDecodeMaxTokens = 1 << 20;         // cache capacity per sequence, at most
