@@ -501,14 +501,16 @@ __device__ inline float group_sum(float x) {
   return x;
 }
 
-// A row of n > 0 kept tokens as 64-token blocks, dealt to the grid's nsg waves per row in equal runs:
+// A row of n kept tokens as 64-token blocks, dealt to the grid's nsg >= 1 waves per row in equal runs:
 // attend_run blocks per wave, the fewest any split over nsg waves can give the busiest one, and
-// attend_waves waves, the fewest that take that run length (the last may take fewer blocks).
+// attend_waves waves, the fewest that take that run length (the last may take fewer blocks); a row
+// with no kept token (a stopped sequence) has none.
 __device__ inline int attend_run(int nsg, int n) {
   const int nblk = (n + 63) / 64;
   return (nblk + nsg - 1) / nsg;
 }
 __device__ inline int attend_waves(int nsg, int n) {
+  if (n <= 0) return 0;
   const int nblk = (n + 63) / 64, run = attend_run(nsg, n);
   return (nblk + run - 1) / run;
 }
