@@ -1,5 +1,5 @@
-"""The benchmark's bookkeeping (CPU): the kept-FLOP count behind the roofline fraction, and the
-refusal of a multi-GPU run.
+"""The benchmark's bookkeeping (CPU): the kept-FLOP count behind the roofline fraction, the stage
+byte counts against the sizes of the arrays they stand for, and the refusal of a multi-GPU run.
 
 bench.kept_flops counts 4·d FLOPs (QK^T and PV, a multiply-add each) per kept (query, key) pair from a
 block list, per chunk row.  It is checked against the token-level keep mask the oracle builds by
@@ -59,3 +59,23 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode != 0 and "one GPU" in r.stderr and r.stdout.strip() == ""
+
+
+def test_stage_bytes_match_the_arrays_moved():
+    """Stage 1 reads Q and K once and writes both summaries; stage 2 reads the summaries, the row
+    pointers and the per-chunk sequence starts and writes the block list: the formula against the
+    sizes of those arrays for a bf16 and an fp32 workload."""
+    for dtype in ("bf16", "f32"):
+        w = W.make_workload([SeqSpec(200, ("uniform", 8, 40), 0, 0), SeqSpec(90, ("uniform", 4, 30), 0, 0)],
+                            8, 2, 32, dtype, seed=14, name="acct")
+        qs = oracle.chunk_summaries(w.q_f32(), w.cu_chunks).astype(np.float32)
+        ks = oracle.chunk_summaries(w.k_f32(), w.cu_chunks).astype(np.float32)
+        rp, bidx, _ = oracle.route(qs, ks, w.seq_chunk_start, np.full(w.total_chunks, 2, np.int32))
+        bidx = bidx.astype(np.int32)
+        s = 2 if dtype == "bf16" else 4
+        b1, b2 = bench.stage_bytes(w.total_tokens, w.total_chunks, w.num_q_heads, w.num_kv_heads, w.head_dim, s,
+                                   bidx.shape[1])
+        assert w.q.dtype.itemsize == s and w.k.dtype.itemsize == s
+        assert b1 == w.q.nbytes + w.k.nbytes + qs.nbytes + ks.nbytes
+        per_chunk_seq_start = np.zeros(w.total_chunks, np.int32)        # one int per chunk
+        assert b2 == qs.nbytes + ks.nbytes + rp.astype(np.int32).nbytes + per_chunk_seq_start.nbytes + bidx.nbytes
