@@ -34,6 +34,8 @@ import sys
 import tempfile
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+from bench_traffic import per_dispatch  # noqa: E402  (sums a counter's rows per dispatch of the named kernels)
 PREFILL_SRC = os.path.join(ROOT, "dynamic_sparse_attention_dhsa_amd", "csrc", "prefill_bf16.hip")
 XCDS, SIMDS, WAVE_SLOTS = 8, 1024, 2          # MI355X: 8 XCDs, 256 CUs x 4 SIMDs; two prefill waves per SIMD
 PASSES = {
@@ -62,15 +64,6 @@ def rocprof_pass(counters: list[str], cmd: list[str], out_dir: str, timeout: int
             rows += list(csv.DictReader(fh))
     bench = [line for line in res.stdout.splitlines() if line.startswith("{")]
     return rows, (json.loads(bench[-1]) if bench else None)
-
-
-def per_dispatch(rows, counter: str, name_filter):
-    acc: dict[int, float] = {}
-    for r in rows:
-        if r["Counter_Name"] != counter or not name_filter(r["Kernel_Name"]):
-            continue
-        acc[int(r["Dispatch_Id"])] = acc.get(int(r["Dispatch_Id"]), 0.0) + float(r["Counter_Value"])
-    return [acc[k] for k in sorted(acc)]
 
 
 def main() -> int:
