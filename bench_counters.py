@@ -71,7 +71,6 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--timeout", type=int, default=240)
     args = ap.parse_args()
-    sys.path.insert(0, ROOT)
     from dynamic_sparse_attention_dhsa_amd import workloads as W
     w = W.make_config(args.config, layout_only=True)
     if w.dtype != "bf16":
