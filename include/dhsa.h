@@ -327,7 +327,11 @@ dhsa_status dhsa_decode_step(const dhsa_decode_state* state, const void* q, cons
  *   Calls on one GPU share its array: calls that may overlap in time (on
  *   different streams or from different threads) race and must not be made;
  *   calls in one stream's order are safe.  Nothing in the array needs to start
- *   at zero: every word a step reads was written earlier in the same step. */
+ *   at zero: every value a step uses was written earlier in the same step (the
+ *   combine also loads partial-state slots that no attention wave wrote in this
+ *   step, and discards them unused).  The first call on a GPU looks up the
+ *   array's address and the attention kernel's occupancy there; a graph capture
+ *   should come after a first call made outside it. */
 #define DHSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 dhsa_status dhsa_decode_step_noalloc(const dhsa_decode_state* state, const void* q, const void* k,
                                      const void* v, int32_t lo, int32_t hi, float tau, int32_t topk,
