@@ -280,3 +280,12 @@ def test_rows_longer_than_the_slice_grid():
             err = np.abs(out[h] - ref).max()
             assert err <= OUT_ATOL[dt], (t, h, err)
     assert longest > (topk + 1) * hi and longest > 2 * 256     # several slices for one wave
+
+
+def test_decode_more_rows_than_resident_waves():
+    """More (sequence, q head) rows than attention waves the GPU holds at once (routing per query head at
+    d = 64: 272 x 16 = 4352 rows, against 4096 resident waves of that kernel on a 256-CU part): the grid
+    then gives each row one wave, which takes all of the row's kept tokens (several 64-token blocks,
+    128 at a time), and the combine reads one partial state per row.  Every sequence against the oracle."""
+    seqs = [SeqSpec(404, ("uniform", 48, 160), 0, 0)] * 272
+    _check(seqs, 16, 4, 64, "bf16", 63, 400, 48, 256, 0.5, 3, grouped=False)
